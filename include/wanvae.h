@@ -1,0 +1,164 @@
+/*
+ * wanvae.h -- C ABI of the MI355X (gfx950) Wan2.2 TI2V-5B VAE decoder.
+ *
+ * The operation is the decoder of FastVideo's "wan22_vae_decode reference.py" page
+ * (a standalone reference of diffusers' AutoencoderKLWan._decode): latents
+ * z [B, 48, T, h, w] -> video [B, 3, 4T-3, 16h, 16w] in [-1, 1], decoded one latent
+ * frame at a time with the causal caches (sections "What is computed", "The parts",
+ * "The first latent frame yields one frame", "Causal caches", "Precision").
+ *
+ * Conventions shared by every entry point
+ *  - All data pointers (z, video, x, cache, y, weight data, workspace) are DEVICE
+ *    pointers on the current HIP device, owned by the caller. The library never frees
+ *    them and keeps no reference after the call returns.
+ *  - Calls are stream-ordered and asynchronous: `stream` is a hipStream_t (NULL = the
+ *    null stream). A status of WANVAE_OK means every launch was enqueued; results are
+ *    ready once the stream is synchronised.
+ *  - dtype is the compute type: WANVAE_F32 (fp32 everywhere) or WANVAE_BF16 (bf16
+ *    operands and storage, fp32 accumulation, at the rounding points the page's
+ *    "Precision" section lists). Any other value -> WANVAE_EDTYPE (the page's ValueError).
+ *    Weights of either dtype are accepted and rounded (nearest even) to the compute type.
+ *  - Arguments are validated before anything is launched: on an error nothing has been
+ *    enqueued. After an error the output contents are undefined.
+ *  - Status codes are 0 or negative; wanvae_last_error() returns a message for the last
+ *    failed call on the calling thread.
+ *  - Workspace: `workspace` may be NULL, in which case the library allocates what it
+ *    needs stream-ordered on `stream` (hipMallocAsync / hipFreeAsync). Otherwise it must
+ *    hold at least the size the matching *_workspace_size function reports; smaller ->
+ *    WANVAE_EWORKSPACE. One workspace must not be used by two calls that overlap in time.
+ */
+#ifndef WANVAE_H
+#define WANVAE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types (wanvae_tensor.dtype, z_dtype and the compute dtype). */
+#define WANVAE_F32 0
+#define WANVAE_BF16 1
+
+/* Activation layouts for the single-op entry points. */
+#define WANVAE_NCTHW 0 /* [B, C, T, H, W], as on the page */
+#define WANVAE_NTHWC 1 /* [B, T, H, W, C], channels last */
+
+/* Status codes. */
+#define WANVAE_OK 0
+#define WANVAE_EDTYPE -1    /* dtype not WANVAE_F32 / WANVAE_BF16 */
+#define WANVAE_EMISSING -2  /* a parameter the decoder needs is not in the table */
+#define WANVAE_ESHAPE -3    /* a size or a parameter shape does not fit */
+#define WANVAE_ETOPOLOGY -4 /* the parameter table is not a Wan2.2 decoder */
+#define WANVAE_EWORKSPACE -5 /* workspace smaller than required */
+#define WANVAE_EHIP -6      /* a HIP call failed (possibly an earlier asynchronous fault) */
+#define WANVAE_EARG -7      /* NULL pointer, duplicate name or other invalid argument */
+
+/* One parameter: diffusers' name, a device pointer to contiguous data, its element type
+ * and shape (ndim <= 5). */
+typedef struct {
+  const char *name;
+  const void *data;
+  int32_t dtype;
+  int32_t ndim;
+  int64_t shape[5];
+} wanvae_tensor;
+
+/*
+ * wanvae_decode -- the whole decoder (the page's decode(z, weights, dtype)).
+ *
+ *  z        [B, 48, T, h, w] NCTHW, element type z_dtype (rounded to dtype first).
+ *  weights  n_weights parameters. Names beginning with "decoder." or "post_quant_conv."
+ *           are used; all others are ignored. The 110 tensors of the decoder must be
+ *           present (else WANVAE_EMISSING) with the shapes of diffusers' state dict
+ *           (else WANVAE_ESHAPE): conv3d weights [Co, Ci, kt, kh, kw], conv2d weights
+ *           [Co, Ci, kh, kw], biases [Co], RMS-norm gammas with C elements in any shape.
+ *           The channel widths (decoder_base_dim) are taken from the shapes; anything
+ *           other than the Wan2.2 layout (z_dim 48, widths 4b, 4b, 4b, 2b, b, 3 residual
+ *           blocks per up block, temporal upsampling in up blocks 0 and 1, patch 2) is
+ *           WANVAE_ETOPOLOGY. Duplicate names -> WANVAE_EARG.
+ *  video    output [B, 3, 4T-3, 16h, 16w] NCTHW of element type dtype, values in [-1, 1]
+ *           (NaN propagates).
+ *  Requires B >= 1, T >= 1, h >= 1, w >= 1, every width <= 1024 and a multiple of 8.
+ */
+int wanvae_decode_workspace_size(int64_t B, int64_t T, int64_t h, int64_t w,
+                                 const wanvae_tensor *weights, int64_t n_weights,
+                                 int32_t dtype, size_t *bytes);
+int wanvae_decode(const void *z, int32_t z_dtype, int64_t B, int64_t T, int64_t h, int64_t w,
+                  const wanvae_tensor *weights, int64_t n_weights, int32_t dtype,
+                  void *video, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * wanvae_causal_conv3d -- one causal conv (WanCausalConv3d, "The parts": causal conv)
+ * of a chunk x with n_cache frames of history:
+ *   y[b,o,t,y,x] = bias[o] + sum_{i,dt,dy,dx} W[o,i,dt,dy,dx] * xt[b,i,t+dt,y+dy-kh/2,x+dx-kw/2]
+ * where xt is (2*(kt/2) - n_cache) zero frames, then the cache frames, then x, with zero
+ * padding kh/2, kw/2 in space.
+ *
+ *  x       [B, Cin, t, h, w] (NCTHW) or [B, t, h, w, Cin] (NTHWC), element type dtype.
+ *  cache   n_cache frames in the same layout ([B, Cin, n_cache, h, w] / [B, n_cache, h, w,
+ *          Cin]), dtype; may be NULL when n_cache == 0. Requires 0 <= n_cache <= 2 and
+ *          n_cache == 0 when kt == 1. In NTHWC both are read in place.
+ *  weight  [Cout, Cin, kt, kh, kw] with kt in {1, 3}, kh, kw in {1, 3}; bias [Cout].
+ *  y       [B, Cout, t, h, w] / [B, t, h, w, Cout], dtype.
+ *  Requires Cin a multiple of 8, t <= 6.
+ */
+int wanvae_causal_conv3d_workspace_size(int64_t B, int64_t Cin, int64_t Cout, int64_t t, int64_t h,
+                                        int64_t w, int64_t n_cache, int32_t layout, int32_t dtype,
+                                        size_t *bytes);
+int wanvae_causal_conv3d(const void *x, const void *cache, int64_t B, int64_t Cin, int64_t t,
+                         int64_t h, int64_t w, int64_t n_cache, const wanvae_tensor *weight,
+                         const wanvae_tensor *bias, int32_t layout, int32_t dtype, void *y,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * wanvae_attn_block -- the mid-block attention block (WanAttentionBlock, "The parts":
+ * attention), per frame of x [B, C, T, h, w]: n = RMS norm of x over channels (times
+ * sqrt(C) and gamma); q, k, v = channels [0,C), [C,2C), [2C,3C) of a 1x1 conv C -> 3C
+ * of n; O = softmax(q k^T / sqrt(C)) v over the h*w positions of the frame (one head of
+ * dim C: the (N*T, H*W, 1, C) layout of MaxDiffusion PR #514's fix); y = proj(O) + x.
+ *
+ *  x       [B, C, T, h, w] (NCTHW) or [B, T, h, w, C] (NTHWC), dtype.
+ *  gamma   C elements; qkv_w [3C, C, 1, 1] (or [3C, C]); qkv_b [3C];
+ *          proj_w [C, C, 1, 1] (or [C, C]); proj_b [C].
+ *  y       same shape and layout as x. Must not alias x.
+ *  Requires C a multiple of 64 and <= 1024.
+ */
+int wanvae_attn_block_workspace_size(int64_t B, int64_t C, int64_t T, int64_t h, int64_t w,
+                                     int32_t layout, int32_t dtype, size_t *bytes);
+int wanvae_attn_block(const void *x, int32_t layout, int64_t B, int64_t C, int64_t T, int64_t h,
+                      int64_t w, const wanvae_tensor *gamma, const wanvae_tensor *qkv_w,
+                      const wanvae_tensor *qkv_b, const wanvae_tensor *proj_w,
+                      const wanvae_tensor *proj_b, int32_t dtype, void *y, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/*
+ * Kernel timing, for measurement. While enabled on a thread, every kernel the library
+ * enqueues from that thread is bracketed by two HIP events recorded on the launch's stream,
+ * and the launch's algorithmic work is noted: FLOPs of a conv (2 * outputs * Cin * kh * kw
+ * * the time taps that fall on real frames; taps on a missing history frame are not
+ * counted), FLOPs of the attention core (4 * S^2 * C per frame), bytes of a norm pass (its
+ * input read once and output written once). wanvae_profile_enable(1) clears the records;
+ * wanvae_profile_read(kind, ...) waits for the recorded events and returns, for the kernel
+ * kind WANVAE_K*, the summed event time in ms, the launch count, and the summed FLOPs and
+ * bytes. Any argument pointer may be NULL.
+ */
+#define WANVAE_KCONV 0
+#define WANVAE_KNORM 1
+#define WANVAE_KATTN 2
+#define WANVAE_KOTHER 3
+int wanvae_profile_enable(int on);
+int wanvae_profile_read(int kind, double *ms, int64_t *launches, double *flops, double *bytes);
+
+/* Message for the last failed call on this thread ("" if none). Valid until the next call. */
+const char *wanvae_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int wanvae_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WANVAE_H */

@@ -1,0 +1,95 @@
+"""Parity of wanvae_attn_block (the mid-block attention block) with the oracle.
+
+The block returns x + branch with branch = proj(softmax(q k^T / sqrt(C)) v). x dominates
+the output, so the branch (out - x) is also compared relative to its own size: fp32 to 1e-5,
+bf16 to 1.5e-2 (every output also within 3e-2 or two bf16 spacings at its magnitude). The oracle
+keeps the softmax probabilities exact; the bf16 kernel rounds them to bf16 for the MFMA.
+A "peaked" variant scales q by 8 so the softmax concentrates on few keys.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+from _gpu import bf16_ulp, dev, rounded, say, to_dev, to_np
+from video_vae_decoding_amd import wanvae
+
+pytestmark = pytest.mark.gpu
+
+
+def weights(g, C, peaked):
+    gm = (1 + 0.1 * g.standard_normal((C, 1, 1))).astype(np.float32)
+    wq = (g.standard_normal((3 * C, C, 1, 1)) / np.sqrt(C)).astype(np.float32)
+    if peaked:
+        wq[:C] *= 8
+    bq = (g.standard_normal(3 * C) / np.sqrt(C)).astype(np.float32)
+    wp = (g.standard_normal((C, C, 1, 1)) / np.sqrt(C)).astype(np.float32)
+    bp = (g.standard_normal(C) / np.sqrt(C)).astype(np.float32)
+    return gm, wq, bq, wp, bp
+
+
+def run(x, ws, mode, layout):
+    xt = to_dev(x, mode)
+    if layout == "nthwc":
+        xt = xt.permute(0, 2, 3, 4, 1).contiguous()
+    y = wanvae.wanvae_attn_block(xt, *[to_dev(a, mode) for a in ws], layout=layout)
+    torch.cuda.synchronize()
+    y = to_np(y)
+    return y.transpose(0, 4, 1, 2, 3) if layout == "nthwc" else y
+
+
+def compare(got, x, ws, mode, what):
+    xr = rounded(x, mode)
+    want = oracle.attention(xr, *[rounded(a, mode) for a in ws], oracle.Prec(mode))
+    d = np.abs(got.astype(np.float64) - want)
+    br = want.astype(np.float64) - xr
+    rel = np.linalg.norm(got - want) / np.linalg.norm(br)
+    say(what, "max", d.max(), "branch rel", rel)
+    if mode == "fp32":
+        assert d.max() <= 1e-4 * max(1.0, np.abs(br).max()), d.max()
+        assert rel <= 1e-5
+    else:
+        # the output x + branch is rounded to bf16 at its own magnitude (outside [-1, 1] one
+        # spacing can exceed 3e-2); the branch itself must agree to 1.5%
+        lim = np.maximum(3e-2, 2 * bf16_ulp(np.abs(want)))
+        assert np.all(d <= lim), d.max()
+        assert rel <= 1.5e-2, rel
+
+
+@pytest.mark.parametrize("mode", ["fp32", "bf16"])
+@pytest.mark.parametrize("layout", ["ncthw", "nthwc"])
+@pytest.mark.parametrize("C,T,h,w,B,peaked", [(64, 3, 4, 5, 2, False), (64, 2, 6, 9, 1, True),
+                                               (128, 2, 7, 11, 1, False), (256, 1, 9, 8, 1, True),
+                                               (1024, 2, 5, 13, 1, False)])
+def test_attn_small(C, T, h, w, B, peaked, layout, mode):
+    say("attn", C, T, h, w, B, peaked, layout, mode)
+    g = np.random.default_rng(C + T + h + w)
+    x = g.standard_normal((B, C, T, h, w)).astype(np.float32)
+    ws = weights(g, C, peaked)
+    compare(run(x, ws, mode, layout), x, ws, mode, f"C{C} {h}x{w} {layout} {mode}")
+
+
+def test_attn_single_position_is_proj_v_plus_x():
+    """One position per frame: softmax over a single key is 1 (MaxDiffusion PR #514's identity)."""
+    g = np.random.default_rng(3)
+    C = 64
+    x = g.standard_normal((2, C, 3, 1, 1)).astype(np.float32)
+    ws = weights(g, C, True)
+    got = run(x, ws, "fp32", "ncthw")
+    compare(got, x, ws, "fp32", "S=1")
+
+
+@pytest.mark.parametrize("mode", ["bf16", "fp32"])
+def test_attn_full_size_sampled_frames(mode):
+    cfg = synthetic.ATTN_CONFIGS["attn1024_31f"]
+    say("attn full", mode)
+    t = cfg.tensors()
+    x = t["x"]
+    ws = [t[k] for k in ("gamma", "qkv_w", "qkv_b", "proj_w", "proj_b")]
+    xt = to_dev(x, mode).permute(0, 2, 3, 4, 1).contiguous()
+    y = wanvae.wanvae_attn_block(xt, *[to_dev(a, mode) for a in ws], layout="nthwc")
+    torch.cuda.synchronize()
+    for f in (0, 17, 30):
+        got = to_np(y[:, f:f + 1]).transpose(0, 4, 1, 2, 3)
+        compare(got, x[:, :, f:f + 1], ws, mode, f"frame {f} {mode}")

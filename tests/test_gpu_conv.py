@@ -1,0 +1,115 @@
+"""Parity of wanvae_causal_conv3d (one causal conv with its cached history) with the oracle.
+
+Small ragged shapes (several tiles, partial tiles in channels, positions and K) are compared
+element by element; the two full-size convs on sampled outputs, each an oracle dot product.
+fp32: |gpu - oracle| within the probabilistic float32 summation bound 8 sqrt(K) 2^-24 sum|w x|.
+bf16: within one bf16 spacing of the oracle's rounded result plus that bound (the float32 sums
+before the rounding may differ by it), almost all bit-equal.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+from _gpu import acc_bound, assert_bf16_close, dev, rounded, say, to_dev, to_np
+from video_vae_decoding_amd import wanvae
+
+pytestmark = pytest.mark.gpu
+
+# (Cin, Cout, kt, kh, kw, t, h, w, n_cache, B)
+SMALL = [
+    (40, 20, 3, 3, 3, 3, 5, 7, 2, 2),
+    (136, 144, 3, 3, 3, 2, 9, 30, 1, 1),
+    (64, 32, 3, 1, 1, 4, 6, 6, 0, 1),
+    (48, 48, 1, 1, 1, 3, 4, 5, 0, 2),
+    (32, 64, 1, 3, 3, 2, 7, 5, 0, 1),
+    (256, 12, 3, 3, 3, 4, 8, 8, 2, 1),
+    (64, 256, 3, 3, 3, 1, 3, 50, 2, 1),
+]
+
+
+def run_gpu(x, cache, w, b, mode, layout):
+    xt, wt, bt = to_dev(x, mode), to_dev(w, mode), to_dev(b, mode)
+    ct = to_dev(cache, mode) if cache is not None and cache.shape[2] else None
+    if layout == "nthwc":
+        xt = xt.permute(0, 2, 3, 4, 1).contiguous()
+        ct = ct.permute(0, 2, 3, 4, 1).contiguous() if ct is not None else None
+    y = wanvae.wanvae_causal_conv3d(xt, ct, wt, bt, layout=layout)
+    torch.cuda.synchronize()
+    y = to_np(y)
+    return y.transpose(0, 4, 1, 2, 3) if layout == "nthwc" else y
+
+
+def check(got, x, cache, w, b, mode, what):
+    P = oracle.Prec(mode)
+    xr, cr, wr, br = (rounded(a, mode) if a is not None else None for a in (x, cache, w, b))
+    hist = cr if cr is not None and cr.shape[2] else None
+    want = oracle.causal_conv(xr, wr, br, hist, P)
+    mag = oracle.causal_conv(np.abs(xr), np.abs(wr), np.abs(br), None if hist is None else np.abs(hist), oracle.Prec("fp64"))
+    err = acc_bound(w[0].size, mag)
+    if mode == "fp32":
+        d = np.abs(got.astype(np.float64) - want)
+        assert np.all(d <= err + 2.0 ** -24 * np.abs(want)), f"{what}: max diff {d.max():.3g}"
+        assert d.max() <= 1e-3
+    else:
+        assert_bf16_close(got, want, err, what=what)
+
+
+@pytest.mark.parametrize("mode", ["fp32", "bf16"])
+@pytest.mark.parametrize("layout", ["ncthw", "nthwc"])
+@pytest.mark.parametrize("case", SMALL)
+def test_conv_small(case, layout, mode):
+    Ci, Co, kt, kh, kw, t, h, w, nc, B = case
+    say("conv", case, layout, mode)
+    g = np.random.default_rng(abs(hash(case)) % 2**31)
+    x = g.standard_normal((B, Ci, t, h, w)).astype(np.float32)
+    cache = g.standard_normal((B, Ci, nc, h, w)).astype(np.float32) if nc else None
+    wgt = (g.standard_normal((Co, Ci, kt, kh, kw)) / np.sqrt(Ci * kt * kh * kw)).astype(np.float32)
+    b = (0.1 * g.standard_normal(Co)).astype(np.float32)
+    got = run_gpu(x, cache, wgt, b, mode, layout)
+    check(got, x, cache, wgt, b, mode, f"{case} {layout} {mode}")
+
+
+def test_conv_is_deterministic_and_zero_history_equals_no_history():
+    g = np.random.default_rng(5)
+    x = g.standard_normal((1, 64, 2, 6, 40)).astype(np.float32)
+    w = (g.standard_normal((128, 64, 3, 3, 3)) / 40).astype(np.float32)
+    b = np.zeros(128, np.float32)
+    a1 = run_gpu(x, None, w, b, "bf16", "nthwc")
+    a2 = run_gpu(x, None, w, b, "bf16", "nthwc")
+    z = run_gpu(x, np.zeros((1, 64, 2, 6, 40), np.float32), w, b, "bf16", "nthwc")
+    assert np.array_equal(a1, a2) and np.array_equal(a1, z)
+
+
+def sample_points(shape, n, seed):
+    g = np.random.default_rng(seed)
+    B, Co, t, h, w = shape
+    pts = np.stack([g.integers(0, s, n) for s in (B, Co, t, h, w)], 1)
+    # the borders, where the padding matters
+    edge = np.array([[0, c, tt, y, xx] for c in (0, Co - 1) for tt in (0, t - 1) for y in (0, h - 1) for xx in (0, w - 1)])
+    return np.concatenate([pts, edge])
+
+
+@pytest.mark.parametrize("mode", ["bf16", "fp32"])
+@pytest.mark.parametrize("name", list(synthetic.CONV_CONFIGS))
+def test_conv_full_size_sampled(name, mode):
+    cfg = synthetic.CONV_CONFIGS[name]
+    say("conv full", name, mode)
+    x, cache, w, b = cfg.tensors()
+    xt = to_dev(x, mode).permute(0, 2, 3, 4, 1).contiguous()
+    ct = to_dev(cache, mode).permute(0, 2, 3, 4, 1).contiguous()
+    y = wanvae.wanvae_causal_conv3d(xt, ct, to_dev(w, mode), to_dev(b, mode), layout="nthwc")
+    torch.cuda.synchronize()
+    pts = sample_points((1, cfg.C, cfg.t, cfg.h, cfg.w), 3000, 77)
+    got = y[pts[:, 0], pts[:, 2], pts[:, 3], pts[:, 4], pts[:, 1]].float().cpu().numpy()
+    xs = np.concatenate([rounded(cache, mode), rounded(x, mode)], 2)
+    want = oracle.conv_points(xs, rounded(w, mode), rounded(b, mode), pts)
+    wr = rounded(w, mode)
+    err = acc_bound(wr[0].size, oracle.conv_points(np.abs(xs), np.abs(wr), np.abs(rounded(b, mode)), pts))
+    if mode == "bf16":
+        assert_bf16_close(got, oracle.round_bf16(want), err, min_exact=0.97, what=name)
+    else:
+        d = np.abs(got - want)
+        assert np.all(d <= err + 2.0 ** -24 * np.abs(want)), d.max()
+        assert d.max() <= 1e-3, d.max()

@@ -1,0 +1,164 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point include/wanvae.h
+declares, and rejects bad arguments with the documented status before launching anything
+(validation never dereferences the data pointers, so host pointers stand in for device ones)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import synthetic
+from video_vae_decoding_amd import wanvae as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "wanvae.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(wanvae_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert {"wanvae_decode", "wanvae_causal_conv3d", "wanvae_attn_block", "wanvae_last_error"} <= set(names)
+    L = W.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.wanvae_version() >= 100
+
+
+def host_weights(base=16):
+    # host tensors: only shapes, dtypes and pointers are read by the validation
+    return {k: torch.zeros(s) for k, s in synthetic.weight_shapes(base).items()}
+
+
+def ws_size(weights, dtype=W.F32, B=1, T=2, h=4, w=4):
+    arr, n = W.tensor_table(weights)
+    out = ctypes.c_size_t(0)
+    rc = W.lib().wanvae_decode_workspace_size(B, T, h, w, arr, n, dtype, ctypes.byref(out))
+    return rc, out.value
+
+
+def test_workspace_size_grows_with_the_problem():
+    wts = host_weights()
+    rc, small = ws_size(wts)
+    assert rc == W.OK and small > 0
+    assert ws_size(wts, T=5)[1] > small
+    assert ws_size(wts, B=2)[1] > small
+    assert ws_size(wts, dtype=W.BF16)[1] < small
+
+
+def full_table(base=256):
+    """A parameter table with the full decoder's shapes and dummy pointers (nothing is read)."""
+    items = list(synthetic.weight_shapes(base).items())
+    tab = (W.wanvae_tensor * len(items))()
+    for i, (k, s) in enumerate(items):
+        tab[i] = W.wanvae_tensor(k.encode(), 4096, W.F32, len(s), (ctypes.c_int64 * 5)(*s, *([0] * (5 - len(s)))))
+    return tab, len(items)
+
+
+def test_decode_workspace_for_the_full_decoder_fits_one_gpu():
+    tab, n = full_table()
+    out = ctypes.c_size_t(0)
+    assert W.lib().wanvae_decode_workspace_size(1, 31, 44, 80, tab, n, W.BF16, ctypes.byref(out)) == W.OK
+    assert 5e9 < out.value < 40e9, out.value
+    assert W.lib().wanvae_decode_workspace_size(2, 31, 44, 80, tab, n, W.F32, ctypes.byref(out)) == W.OK
+    assert out.value < 150e9, out.value
+
+
+def call_decode(weights, dtype=W.F32, z_dtype=W.F32, B=1, T=2, h=4, w=4, z=4096, video=4096, ws=4096, ws_bytes=1 << 40):
+    arr, n = W.tensor_table(weights)
+    return W.lib().wanvae_decode(z, z_dtype, B, T, h, w, arr, n, dtype, video, ws, ws_bytes, None)
+
+
+def test_bad_dtype_is_edtype():
+    assert call_decode(host_weights(), dtype=2) == W.EDTYPE
+    assert "WANVAE_F32" in W.lib().wanvae_last_error().decode()
+    assert call_decode(host_weights(), z_dtype=7) == W.EDTYPE
+    with pytest.raises(ValueError):
+        W.check(W.EDTYPE)
+
+
+def test_missing_parameter_is_emissing():
+    wts = host_weights()
+    del wts["decoder.up_blocks.1.upsampler.time_conv.bias"]
+    assert call_decode(wts) == W.EMISSING
+    assert "time_conv.bias" in W.lib().wanvae_last_error().decode()
+
+
+def test_wrong_shape_is_eshape():
+    wts = host_weights()
+    wts["decoder.mid_block.resnets.1.conv2.weight"] = torch.zeros(64, 64, 3, 3, 1)
+    assert call_decode(wts) == W.ESHAPE
+    wts = host_weights()
+    wts["decoder.norm_out.gamma"] = torch.zeros(15)
+    assert call_decode(wts) == W.ESHAPE
+    assert call_decode(host_weights(), T=0) == W.ESHAPE
+
+
+def test_gamma_of_any_shape_with_C_elements_is_accepted():
+    wts = host_weights()
+    wts["decoder.norm_out.gamma"] = torch.zeros(16)
+    wts["decoder.mid_block.attentions.0.norm.gamma"] = torch.zeros(1, 64)
+    assert ws_size(wts)[0] == W.OK
+
+
+def test_other_topology_is_etopology():
+    assert call_decode(host_weights(base=8)) == W.ETOPOLOGY
+    wts = host_weights()
+    wts["post_quant_conv.weight"] = torch.zeros(16, 16, 1, 1, 1)
+    assert call_decode(wts) == W.ETOPOLOGY
+
+
+def test_duplicate_names_and_null_pointers_are_earg():
+    wts = host_weights()
+    arr, n = W.tensor_table(wts)
+    dup = (W.wanvae_tensor * (n + 1))(*arr[:n], arr[0])
+    assert W.lib().wanvae_decode(4096, 0, 1, 2, 4, 4, dup, n + 1, 0, 4096, 4096, 1 << 40, None) == W.EARG
+    assert call_decode(wts, z=None) == W.EARG
+
+
+def test_names_outside_the_prefixes_are_ignored():
+    wts = host_weights()
+    wts["encoder.conv_in.weight"] = torch.zeros(3)
+    wts["encoder.conv_in.weight2"] = torch.zeros(3)
+    assert ws_size(wts)[0] == W.OK
+
+
+def test_small_workspace_is_eworkspace():
+    wts = host_weights()
+    _, need = ws_size(wts)
+    assert call_decode(wts, ws_bytes=need - 1) == W.EWORKSPACE
+
+
+def test_conv_and_attention_validation():
+    L = W.lib()
+    w = W.tensor_struct("weight", torch.zeros(16, 24, 3, 3, 3))
+    b = W.tensor_struct("bias", torch.zeros(16))
+    args = dict(x=4096, cache=4096, B=1, Cin=24, t=2, h=4, w=4, n=2)
+
+    def conv(**kw):
+        a = {**args, **kw}
+        return L.wanvae_causal_conv3d(a["x"], a["cache"], a["B"], a["Cin"], a["t"], a["h"], a["w"], a["n"],
+                                      ctypes.byref(w), ctypes.byref(b), kw.get("layout", 0), kw.get("dtype", 0),
+                                      4096, 4096, 1 << 40, None)
+    assert conv(dtype=3) == W.EDTYPE
+    assert conv(Cin=20) == W.ESHAPE        # not a multiple of 8 / does not match the weight
+    assert conv(n=3) == W.ESHAPE
+    assert conv(t=7) == W.ESHAPE
+    assert conv(cache=None) == W.EARG
+    assert conv(layout=5) == W.EARG
+    g = W.tensor_struct("gamma", torch.zeros(64))
+    qw = W.tensor_struct("qkv_w", torch.zeros(192, 64, 1, 1))
+    qb = W.tensor_struct("qkv_b", torch.zeros(192))
+    pw = W.tensor_struct("proj_w", torch.zeros(64, 64, 1, 1))
+    pb = W.tensor_struct("proj_b", torch.zeros(64))
+
+    def attn(C=64, x=4096, y=8192, dtype=0, gam=g):
+        return L.wanvae_attn_block(x, 0, 1, C, 2, 3, 3, ctypes.byref(gam), ctypes.byref(qw), ctypes.byref(qb),
+                                   ctypes.byref(pw), ctypes.byref(pb), dtype, y, 4096, 1 << 40, None)
+    assert attn(dtype=9) == W.EDTYPE
+    assert attn(C=96) == W.ESHAPE
+    assert attn(y=4096) == W.EARG
+    assert attn(gam=W.tensor_struct("gamma", torch.zeros(63))) == W.ESHAPE

@@ -1,0 +1,95 @@
+// Internal interface between the host orchestrator (wanvae.cpp) and the gfx950 kernels
+// (kernels.hip). Activations live in HBM as channels-last frames: one frame of a
+// level is [B][H][W][C] contiguous, and a kernel addresses frame s through a table of
+// frame pointers (nullptr = a zero frame). The causal caches are therefore read in
+// place: a conv's table lists its history frames, then the chunk's frames, wherever
+// they live.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace wanvae {
+
+constexpr int kMaxFrames = 8;  // 2 history frames + up to 4 chunk frames, or 8 interleaved outputs
+
+enum Dtype { kF32 = 0, kBF16 = 1 };
+
+// Epilogue of the conv kernel: where and how the accumulated result is written.
+enum Epilogue {
+  kEpiFrames = 0,      // out frame t, channel c
+  kEpiInterleave = 1,  // time conv: channel c < outC -> frame 2t, channel outC + c -> frame 2t+1
+  kEpiVideo = 2,       // unpatchify + clamp into the NCTHW video
+  kEpiQKV = 3,         // 1x1 conv C -> 3C: q, k as [frame][S][C], v transposed as [frame][C][Sp]
+};
+
+struct ConvArgs {
+  // input frames of the time-padded sequence (history zeros as nullptr), batch strides in elements
+  const void* in[kMaxFrames];
+  int64_t in_bs[kMaxFrames];
+  int B, Hin, Win, Cin;   // input frame geometry
+  int Ho, Wo, Cout;       // output geometry
+  int kt, kh, kw;         // kernel (kt in {1,3}; kh, kw in {1,3})
+  int up;                 // 1: the input is read through nearest x2 upsampling (Hin = Ho/2)
+  int F;                  // output frames
+  const void* w;          // [Cout][kt][kh][kw][Cin], compute type
+  const float* bias;      // [Cout], value already rounded to the compute type
+  int mode;               // Epilogue
+  void* out[kMaxFrames];
+  int64_t out_bs[kMaxFrames];
+  int outC;               // channels of an output frame (Cout, Cout/2 interleaved, C for QKV)
+  int has_res;            // += residual frame (same layout as out), each sum rounded
+  const void* res[kMaxFrames];
+  int64_t res_bs[kMaxFrames];
+  int has_dup;            // += DupUp3D of the block input at (Ho/2, Wo/2)
+  const void* dup[kMaxFrames];
+  int64_t dup_bs[kMaxFrames];
+  int dup_C, dup_r, dup_ft, dup_shift;
+  void* video;            // kEpiVideo: [B][3][vF][2Ho][2Wo]
+  int vF, vf0;
+  void* q;                // kEpiQKV
+  void* k;
+  void* vt;
+  int S, Sp;
+};
+
+struct NormArgs {
+  const void* in[kMaxFrames];
+  int64_t in_bs[kMaxFrames];
+  void* out[kMaxFrames];
+  int64_t out_bs[kMaxFrames];
+  int F, B, HW, C;
+  const float* gamma;  // [C], rounded to the compute type
+  float sqrtC;         // sqrt(C) as a float
+  int silu;
+};
+
+struct AttnArgs {
+  const void* q;   // [nfr][S][C]
+  const void* k;   // [nfr][S][C]
+  const void* vt;  // [nfr][C][Sp], zero beyond S
+  void* o;         // [nfr][S][C]
+  int nfr, S, Sp, C;
+  float scale;     // 1/sqrt(C)
+};
+
+// Tile shapes of the conv kernel: channels x positions per workgroup.
+enum ConvTile { kTile128x128 = 0, kTile32x256 = 1, kTile256x128 = 2 };
+
+hipError_t launch_conv(const ConvArgs& a, int dtype, int tile, hipStream_t s);
+hipError_t launch_norm(const NormArgs& a, int dtype, hipStream_t s);
+bool attn_supported(int C, int dtype);
+hipError_t launch_attn(const AttnArgs& a, int dtype, hipStream_t s);
+// w [Cout][Cin][taps] (src dtype) -> [Cout][taps][Cin] (dst dtype), rounded to nearest even
+hipError_t launch_repack(const void* w, int src_dtype, void* dst, int dst_dtype, int Cout, int Cin, int taps,
+                         hipStream_t s);
+// n values (src dtype) -> float, rounded to the compute dtype first
+hipError_t launch_to_f32(const void* x, int src_dtype, float* dst, int64_t n, int dtype, hipStream_t s);
+// NCTHW [B][C][T][H][W] (src dtype) -> frames [T][B][H][W][Cp] (dst dtype), channels >= C zero
+hipError_t launch_ncthw_to_frames(const void* x, int src_dtype, void* dst, int dst_dtype, int B, int C, int Cp, int T,
+                                  int H, int W, hipStream_t s);
+// frames [T][B][H][W][C] -> NCTHW [B][C][T][H][W], same dtype
+hipError_t launch_frames_to_ncthw(const void* x, void* dst, int dtype, int B, int C, int T, int H, int W,
+                                  hipStream_t s);
+
+}  // namespace wanvae

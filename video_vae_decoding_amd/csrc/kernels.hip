@@ -1,0 +1,699 @@
+// gfx950 kernels of the Wan2.2 TI2V-5B VAE decoder.
+//
+//  k_conv   implicit-GEMM causal conv (3x3x3, 3x1x1, 3x3 2-D, 1x1) on MFMA: bf16 operands
+//           with fp32 accumulation (v_mfma_f32_16x16x32_bf16) or fp32 (v_mfma_f32_16x16x4f32).
+//           Fused epilogues: bias, residual add, DupUp3D add, the time conv's channel->frame
+//           interleave, unpatchify + clamp, and the q/k/v split of the attention's 1x1 conv.
+//  k_norm   WanRMS_norm (+ SiLU) per position: one wave per position, HBM bound.
+//  k_attn   single-head attention over the h*w positions of a frame, flash style: the head
+//           dim is split across the waves of a workgroup, partial scores are summed through
+//           LDS in a fixed order, online softmax, P kept in registers.
+// Reference for what is computed: FastVideo's "wan22_vae_decode reference.py" page
+// (sections "The parts" and "Precision").
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "internal.h"
+
+namespace wanvae {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+struct bf16_t {
+  uint16_t u;
+};
+
+// ------------------------------------------------------------------ element helpers
+
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// float -> bfloat16, round to nearest even; NaN stays NaN
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <typename T>
+struct Elem;
+template <>
+struct Elem<float> {
+  static __device__ __forceinline__ float ld(const float* p) { return *p; }
+  static __device__ __forceinline__ void st(float* p, float v) { *p = v; }
+  static __device__ __forceinline__ float R(float v) { return v; }
+  static __device__ __forceinline__ void ld4(const float* p, float v[4]) {
+    float4 x = *(const float4*)p;
+    v[0] = x.x, v[1] = x.y, v[2] = x.z, v[3] = x.w;
+  }
+  static __device__ __forceinline__ void st4(float* p, const float v[4]) { *(float4*)p = make_float4(v[0], v[1], v[2], v[3]); }
+};
+template <>
+struct Elem<bf16_t> {
+  static __device__ __forceinline__ float ld(const bf16_t* p) { return bf2f(p->u); }
+  static __device__ __forceinline__ void st(bf16_t* p, float v) { p->u = f2bf(v); }
+  static __device__ __forceinline__ float R(float v) { return bf2f(f2bf(v)); }
+  static __device__ __forceinline__ void ld4(const bf16_t* p, float v[4]) {
+    uint2 x = *(const uint2*)p;
+    v[0] = bf2f(x.x & 0xffff), v[1] = bf2f(x.x >> 16), v[2] = bf2f(x.y & 0xffff), v[3] = bf2f(x.y >> 16);
+  }
+  static __device__ __forceinline__ void st4(bf16_t* p, const float v[4]) {
+    uint2 x;
+    x.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+    x.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+    *(uint2*)p = x;
+  }
+};
+
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2). Renumber
+// them so that each XCD runs a contiguous range of tiles, which share input rows and
+// weight tiles in that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+  constexpr int X = 8;
+  const int q = n / X, r = n % X, xcd = bid % X, idx = bid / X;
+  return xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+}
+
+// One 16x16 MFMA step on a 16-byte fragment pair: bf16 covers 32 k (8 per lane group),
+// fp32 covers 16 k (4 per lane group, one MFMA per component). The k order inside a
+// fragment is the same for both operands, so the sum is the same contraction.
+template <typename T>
+struct Mma;
+template <>
+struct Mma<bf16_t> {
+  static __device__ __forceinline__ void run(f32x4_t& acc, const uint4& a, const uint4& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                  acc, 0, 0, 0);
+  }
+};
+template <>
+struct Mma<float> {
+  static __device__ __forceinline__ void run(f32x4_t& acc, const uint4& a, const uint4& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+  }
+};
+
+// ------------------------------------------------------------------ conv epilogue
+
+// v[0..3]: accumulated sums + bias for output channels c..c+3 at (frame t, batch b, y, x).
+template <typename T>
+__device__ __forceinline__ void conv_epilogue(const ConvArgs& a, int t, int b, int y, int x, int c, float v[4]) {
+  using X = Elem<T>;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = X::R(v[i]);
+  const int64_t pix = (int64_t)y * a.Wo + x;
+  if (a.has_res) {
+    const T* r = (const T*)a.res[t] + b * a.res_bs[t] + pix * a.outC + c;
+    float rv[4];
+    X::ld4(r, rv);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = X::R(v[i] + rv[i]);
+  }
+  if (a.has_dup) {
+    // DupUp3D: dup[c, ft*t + s, 2y + i, 2x + j] = in[(4 ft c + 4 s + 2 i + j) / r, t, y, x]
+    const int ts = t + a.dup_shift, tin = ts / a.dup_ft, sub_t = ts - tin * a.dup_ft;
+    const int Wh = a.Wo >> 1;
+    const T* d = (const T*)a.dup[tin] + b * a.dup_bs[tin] + ((int64_t)(y >> 1) * Wh + (x >> 1)) * a.dup_C;
+    const int sub = 4 * sub_t + 2 * (y & 1) + (x & 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = X::R(v[i] + X::ld(d + (4 * a.dup_ft * (c + i) + sub) / a.dup_r));
+  }
+  if (a.mode == kEpiFrames) {
+    X::st4((T*)a.out[t] + b * a.out_bs[t] + pix * a.outC + c, v);
+  } else if (a.mode == kEpiInterleave) {
+    const int half = c >= a.outC ? 1 : 0, fr = 2 * t + half;
+    X::st4((T*)a.out[fr] + b * a.out_bs[fr] + pix * a.outC + (c - half * a.outC), v);
+  } else if (a.mode == kEpiVideo) {
+    // video[b, k, f, 2y + i, 2x + j] = clamp(out[b, 4k + 2j + i, f, y, x]); NaN passes through
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int cc = c + e;
+      if (cc >= a.Cout) break;
+      const int k = cc >> 2, j = (cc >> 1) & 1, i = cc & 1;
+      const float u = v[e] < -1.f ? -1.f : (v[e] > 1.f ? 1.f : v[e]);
+      T* o = (T*)a.video + ((((int64_t)b * 3 + k) * a.vF + a.vf0 + t) * (2 * a.Ho) + 2 * y + i) * (int64_t)(2 * a.Wo) +
+             2 * x + j;
+      X::st(o, u);
+    }
+  } else {  // kEpiQKV
+    const int C = a.outC, fr = t * a.B + b;
+    if (c < 2 * C) {
+      T* o = (T*)(c < C ? a.q : a.k) + ((int64_t)fr * a.S + pix) * C + (c < C ? c : c - C);
+      X::st4(o, v);
+    } else {
+      T* o = (T*)a.vt + ((int64_t)fr * C + (c - 2 * C)) * a.Sp + pix;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) X::st(o + (int64_t)e * a.Sp, v[e]);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ implicit-GEMM conv
+//
+// GEMM view: D[n][m] = sum_k W[n][k] * A[m][k], n = output channel, m = output position
+// (t, b, y, x), k = (tap, input channel). Each workgroup (4 waves, 2 x 2) computes a TC x TP
+// tile of D. Per K step (one tap, BK input channels = 128 bytes per row) the W and A tiles
+// are staged through LDS (double buffered, one barrier per step): each thread loads 16-byte
+// chunks from HBM/L2 for step s+1 into registers while the MFMAs of step s run. A rows are
+// gathered from the frame table with the tap's shift (zero outside the frame or for a
+// missing history frame), so neither padding nor the cache concatenation is materialised.
+// Weights are the MFMA A operand: every lane then holds 4 consecutive output channels.
+template <typename T, int TC, int TP>
+__global__ void __launch_bounds__(256) k_conv(const ConvArgs a) {
+  constexpr int VEC = 16 / (int)sizeof(T);
+  constexpr int BK = 8 * VEC;
+  constexpr int ROW = 144;  // 128 data bytes + 16 pad: conflict-free 16-byte LDS reads
+  constexpr int NWR = TC / 32, NAR = TP / 32;
+  constexpr int STAGE = (TC + TP) * ROW;
+  constexpr int WC = TC / 2, WP = TP / 2, TCN = WC / 16, TPN = WP / 16;
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int HWo = a.Ho * a.Wo;
+  const int M = a.F * a.B * HWo;
+  const int nct = (a.Cout + TC - 1) / TC;
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int ct = bid % nct, pt = bid / nct;
+  const int c0 = ct * TC, m0 = pt * TP;
+  const int j = tid & 7, r0 = tid >> 3;
+  const int khw = a.kh * a.kw, taps = a.kt * khw;
+  const int csteps = (a.Cin + BK - 1) / BK;
+  const int steps = taps * csteps;
+  const int64_t Ktot = (int64_t)taps * a.Cin;
+  const int ph = a.kh >> 1, pw = a.kw >> 1;
+
+  // per A row: the row's frame pointer for each time tap, and its output (y, x)
+  const T* rb0[NAR];
+  const T* rb1[NAR];
+  const T* rb2[NAR];
+  int ry[NAR], rx[NAR];
+#pragma unroll
+  for (int i = 0; i < NAR; ++i) {
+    const int m = m0 + r0 + 32 * i;
+    rb0[i] = rb1[i] = rb2[i] = nullptr;
+    ry[i] = rx[i] = 0;
+    if (m < M) {
+      const int x = m % a.Wo;
+      int q = m / a.Wo;
+      const int y = q % a.Ho;
+      q /= a.Ho;
+      const int b = q % a.B, t = q / a.B;
+      ry[i] = y;
+      rx[i] = x;
+      const T* p0 = (const T*)a.in[t];
+      rb0[i] = p0 ? p0 + b * a.in_bs[t] : nullptr;
+      if (a.kt > 1) {
+        const T* p1 = (const T*)a.in[t + 1];
+        const T* p2 = (const T*)a.in[t + 2];
+        rb1[i] = p1 ? p1 + b * a.in_bs[t + 1] : nullptr;
+        rb2[i] = p2 ? p2 + b * a.in_bs[t + 2] : nullptr;
+      }
+    }
+  }
+
+  uint4 wr[NWR], ar[NAR];
+  auto gload = [&](int s) {
+    const int tap = s / csteps, cs = s - tap * csteps;
+    const int ci = cs * BK + j * VEC;
+    const int dt = tap / khw, rr = tap - dt * khw, dy = rr / a.kw, dx = rr - dy * a.kw;
+    const bool cok = ci < a.Cin;
+    const T* wb = (const T*)a.w + (int64_t)tap * a.Cin + ci;
+#pragma unroll
+    for (int i = 0; i < NWR; ++i) {
+      const int n = c0 + r0 + 32 * i;
+      wr[i] = (cok && n < a.Cout) ? *(const uint4*)(wb + n * Ktot) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NAR; ++i) {
+      const T* base = dt == 0 ? rb0[i] : (dt == 1 ? rb1[i] : rb2[i]);
+      int yy, xx;
+      bool ok = cok && base != nullptr;
+      if (a.up) {
+        const int yu = ry[i] + dy - ph, xu = rx[i] + dx - pw;
+        ok = ok && yu >= 0 && yu < a.Ho && xu >= 0 && xu < a.Wo;
+        yy = yu >> 1;
+        xx = xu >> 1;
+      } else {
+        yy = ry[i] + dy - ph;
+        xx = rx[i] + dx - pw;
+        ok = ok && yy >= 0 && yy < a.Hin && xx >= 0 && xx < a.Win;
+      }
+      ar[i] = ok ? *(const uint4*)(base + ((int64_t)yy * a.Win + xx) * a.Cin + ci) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto sstore = [&](int buf) {
+    char* sw = smem + buf * STAGE;
+    char* sa = sw + TC * ROW;
+#pragma unroll
+    for (int i = 0; i < NWR; ++i) *(uint4*)(sw + (r0 + 32 * i) * ROW + j * 16) = wr[i];
+#pragma unroll
+    for (int i = 0; i < NAR; ++i) *(uint4*)(sa + (r0 + 32 * i) * ROW + j * 16) = ar[i];
+  };
+
+  const int wc = wave >> 1, wp = wave & 1;
+  f32x4_t acc[TCN][TPN];
+#pragma unroll
+  for (int ic = 0; ic < TCN; ++ic)
+#pragma unroll
+    for (int ip = 0; ip < TPN; ++ip) acc[ic][ip] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int buf) {
+    const char* sw = smem + buf * STAGE + (wc * WC) * ROW;
+    const char* sa = smem + buf * STAGE + TC * ROW + (wp * WP) * ROW;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int off = (sub * 4 + (lane >> 4)) * 16;
+      uint4 wf[TCN], af[TPN];
+#pragma unroll
+      for (int ic = 0; ic < TCN; ++ic) wf[ic] = *(const uint4*)(sw + (ic * 16 + (lane & 15)) * ROW + off);
+#pragma unroll
+      for (int ip = 0; ip < TPN; ++ip) af[ip] = *(const uint4*)(sa + (ip * 16 + (lane & 15)) * ROW + off);
+#pragma unroll
+      for (int ic = 0; ic < TCN; ++ic)
+#pragma unroll
+        for (int ip = 0; ip < TPN; ++ip) Mma<T>::run(acc[ic][ip], wf[ic], af[ip]);
+    }
+  };
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int s = 0; s < steps; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < steps) gload(s + 1);
+    compute(buf);
+    if (s + 1 < steps) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int ip = 0; ip < TPN; ++ip) {
+    const int m = m0 + wp * WP + ip * 16 + (lane & 15);
+    if (m >= M) continue;
+    const int x = m % a.Wo;
+    int q = m / a.Wo;
+    const int y = q % a.Ho;
+    q /= a.Ho;
+    const int b = q % a.B, t = q / a.B;
+#pragma unroll
+    for (int ic = 0; ic < TCN; ++ic) {
+      const int c = c0 + wc * WC + ic * 16 + 4 * (lane >> 4);
+      if (c >= a.Cout) continue;
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = acc[ic][ip][e] + (c + e < a.Cout ? a.bias[c + e] : 0.f);
+      conv_epilogue<T>(a, t, b, y, x, c, v);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ RMS norm (+ SiLU)
+//
+// y = x / max(||x||_2, 1e-12) (rounded), * sqrt(C) (rounded), * gamma (rounded), then
+// optionally SiLU (rounded): the 16-bit chain of the page's "Precision" section; in fp32
+// every rounding is the float32 one. One wave per position, C <= 1024.
+template <typename T>
+__global__ void __launch_bounds__(256) k_norm(const NormArgs a) {
+  using X = Elem<T>;
+  const int lane = threadIdx.x & 63;
+  const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t M = (int64_t)a.F * a.B * a.HW;
+  if (m >= M) return;
+  const int pos = (int)(m % a.HW);
+  const int64_t q = m / a.HW;
+  const int b = (int)(q % a.B), t = (int)(q / a.B);
+  const T* x = (const T*)a.in[t] + b * a.in_bs[t] + (int64_t)pos * a.C;
+  T* y = (T*)a.out[t] + b * a.out_bs[t] + (int64_t)pos * a.C;
+  float v[16];
+  float ss = 0.f;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int c = (it * 64 + lane) * 4;
+    if (c < a.C) {
+      X::ld4(x + c, v + 4 * it);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ss += v[4 * it + e] * v[4 * it + e];
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+  const float d = fmaxf(sqrtf(ss), 1e-12f);
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int c = (it * 64 + lane) * 4;
+    if (c < a.C) {
+      float o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float u = X::R(v[4 * it + e] / d);
+        u = X::R(u * a.sqrtC);
+        u = X::R(u * a.gamma[c + e]);
+        if (a.silu) u = X::R(u / (1.f + expf(-u)));
+        o[e] = u;
+      }
+      X::st4(y + c, o);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ attention
+//
+// One workgroup: 32 queries (2 tiles of 16) of one frame, NW waves; wave w owns head dims
+// [w*DW, (w+1)*DW). Per block of 32 keys each wave computes its partial S^T = K Q^T over its
+// dims (MFMA, Q fragments held in registers), the partials are summed through LDS (wave
+// order fixed, so the result is deterministic), then every wave runs the online softmax on
+// the full scores and accumulates O^T += V^T P for its own dims. S^T's accumulator layout
+// (keys 4g..4g+3 of each 16-key tile in lane group g, one query per lane) is directly the
+// k layout of P as the B operand of the PV MFMA; V^T is read with the same key order.
+template <typename T, int NW, int DW>
+__global__ void __launch_bounds__(64 * NW) k_attn(const AttnArgs a) {
+  using X = Elem<T>;
+  constexpr bool BF = sizeof(T) == 2;
+  constexpr int KS = BF ? 32 : 16;  // head dims per S MFMA step
+  constexpr int NKS = DW / KS;
+  constexpr int NDT = DW / 16;       // 16-dim tiles of O per wave
+  __shared__ f32x4_t red[2][NW][4][64];
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int fr = blockIdx.y, q0 = blockIdx.x * 32;
+  const int C = a.C, S = a.S, Sp = a.Sp;
+  const T* Q = (const T*)a.q + (int64_t)fr * S * C;
+  const T* K = (const T*)a.k + (int64_t)fr * S * C;
+  const T* Vt = (const T*)a.vt + (int64_t)fr * C * Sp;
+  const int dw0 = w * DW;
+  const float sc = a.scale * 1.4426950408889634f;  // softmax in base 2
+
+  uint4 qf[NKS][2];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int qi = min(q0 + qt * 16 + l16, S - 1);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      qf[ks][qt] = *(const uint4*)(Q + (int64_t)qi * C + dw0 + ks * KS + g * (BF ? 8 : 4));
+  }
+  f32x4_t o[NDT][2];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) o[dt][0] = o[dt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
+
+  int par = 0;
+  for (int kv0 = 0; kv0 < S; kv0 += 32, par ^= 1) {
+    f32x4_t s[2][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) s[kt][0] = s[kt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const int key = min(kv0 + kt * 16 + l16, S - 1);
+        const uint4 kf = *(const uint4*)(K + (int64_t)key * C + dw0 + ks * KS + g * (BF ? 8 : 4));
+        Mma<T>::run(s[kt][0], kf, qf[ks][0]);
+        Mma<T>::run(s[kt][1], kf, qf[ks][1]);
+      }
+    }
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) red[par][w][kt * 2 + qt][lane] = s[kt][qt];
+    __syncthreads();
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        f32x4_t t = red[par][0][kt * 2 + qt][lane];
+#pragma unroll
+        for (int ww = 1; ww < NW; ++ww) t += red[par][ww][kt * 2 + qt][lane];
+        s[kt][qt] = t;
+      }
+    // online softmax; key of element e in tile kt: kv0 + kt*16 + 4g + e
+    float p[2][2][4];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = kv0 + kt * 16 + 4 * g + e;
+          const float v = key < S ? s[kt][qt][e] * sc : -INFINITY;
+          p[kt][qt][e] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mnew = fmaxf(mrun[qt], mx);
+      const float alpha = exp2f(mrun[qt] - mnew);
+      float sum = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float pe = exp2f(p[kt][qt][e] - mnew);
+          p[kt][qt][e] = pe;
+          sum += pe;
+        }
+      sum += __shfl_xor(sum, 16, 64);
+      sum += __shfl_xor(sum, 32, 64);
+      lrun[qt] = lrun[qt] * alpha + sum;
+      mrun[qt] = mnew;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[dt][qt] *= alpha;
+    }
+    // O^T[d][q] += V^T[d][key] P^T[key][q]
+    if constexpr (BF) {
+      uint4 pb[2];
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        pb[qt].x = (uint32_t)f2bf(p[0][qt][0]) | ((uint32_t)f2bf(p[0][qt][1]) << 16);
+        pb[qt].y = (uint32_t)f2bf(p[0][qt][2]) | ((uint32_t)f2bf(p[0][qt][3]) << 16);
+        pb[qt].z = (uint32_t)f2bf(p[1][qt][0]) | ((uint32_t)f2bf(p[1][qt][1]) << 16);
+        pb[qt].w = (uint32_t)f2bf(p[1][qt][2]) | ((uint32_t)f2bf(p[1][qt][3]) << 16);
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const T* vrow = Vt + (int64_t)(dw0 + dt * 16 + l16) * Sp + kv0 + 4 * g;
+        const uint2 lo = *(const uint2*)vrow, hi = *(const uint2*)(vrow + 16);
+        const uint4 vf = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        Mma<T>::run(o[dt][0], vf, pb[0]);
+        Mma<T>::run(o[dt][1], vf, pb[1]);
+      }
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const T* vrow = Vt + (int64_t)(dw0 + dt * 16 + l16) * Sp + kv0 + 4 * g;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          const float4 vf = *(const float4*)(vrow + kt * 16);
+          const float vv[4] = {vf.x, vf.y, vf.z, vf.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            o[dt][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv[e], p[kt][0][e], o[dt][0], 0, 0, 0);
+            o[dt][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv[e], p[kt][1][e], o[dt][1], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int qi = q0 + qt * 16 + l16;
+    if (qi >= S) continue;
+    const float inv = 1.f / lrun[qt];
+    T* orow = (T*)a.o + ((int64_t)fr * S + qi) * C + dw0 + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = o[dt][qt][e] * inv;
+      X::st4(orow + dt * 16, v);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ small kernels
+
+template <typename S>
+__device__ __forceinline__ float load_as_f32(const S* p, int64_t i);
+template <>
+__device__ __forceinline__ float load_as_f32<float>(const float* p, int64_t i) {
+  return p[i];
+}
+template <>
+__device__ __forceinline__ float load_as_f32<bf16_t>(const bf16_t* p, int64_t i) {
+  return bf2f(p[i].u);
+}
+
+template <typename S, typename D>
+__global__ void k_repack(const S* w, D* wp, int Cout, int Cin, int taps) {
+  const int64_t n = (int64_t)Cout * Cin * taps;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * blockDim.x) {
+    const int ci = (int)(idx % Cin);
+    const int64_t r = idx / Cin;
+    const int tap = (int)(r % taps);
+    const int64_t o = r / taps;
+    Elem<D>::st(wp + idx, load_as_f32<S>(w, (o * Cin + ci) * taps + tap));
+  }
+}
+
+template <typename S>
+__global__ void k_to_f32(const S* x, float* y, int64_t n, int bf) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const float v = load_as_f32<S>(x, i);
+    y[i] = bf ? bf2f(f2bf(v)) : v;
+  }
+}
+
+template <typename S, typename D>
+__global__ void k_ncthw_to_frames(const S* x, D* y, int B, int C, int Cp, int T, int H, int W) {
+  const int64_t n = (int64_t)T * B * H * W * Cp;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * blockDim.x) {
+    const int c = (int)(idx % Cp);
+    int64_t r = idx / Cp;
+    const int xx = (int)(r % W);
+    r /= W;
+    const int yy = (int)(r % H);
+    r /= H;
+    const int b = (int)(r % B);
+    const int t = (int)(r / B);
+    const float v = c < C ? load_as_f32<S>(x, ((((int64_t)b * C + c) * T + t) * H + yy) * W + xx) : 0.f;
+    Elem<D>::st(y + idx, v);
+  }
+}
+
+template <typename D>
+__global__ void k_frames_to_ncthw(const D* x, D* y, int B, int C, int T, int H, int W) {
+  const int64_t n = (int64_t)B * C * T * H * W;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * blockDim.x) {
+    const int xx = (int)(idx % W);
+    int64_t r = idx / W;
+    const int yy = (int)(r % H);
+    r /= H;
+    const int t = (int)(r % T);
+    r /= T;
+    const int c = (int)(r % C);
+    const int b = (int)(r / C);
+    y[idx] = x[((((int64_t)t * B + b) * H + yy) * W + xx) * C + c];
+  }
+}
+
+// ------------------------------------------------------------------ launchers
+
+static int grid_for(int64_t n, int block) {
+  int64_t g = (n + block - 1) / block;
+  return (int)(g < 65536 ? (g > 0 ? g : 1) : 65536);
+}
+
+template <typename T, int TC, int TP>
+static hipError_t conv_go(const ConvArgs& a, hipStream_t s) {
+  const int64_t M = (int64_t)a.F * a.B * a.Ho * a.Wo;
+  const int64_t blocks = ((a.Cout + TC - 1) / TC) * ((M + TP - 1) / TP);
+  hipLaunchKernelGGL((k_conv<T, TC, TP>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_conv(const ConvArgs& a, int dtype, int tile, hipStream_t s) {
+  if (dtype == kBF16) {
+    if (tile == kTile32x256) return conv_go<bf16_t, 32, 256>(a, s);
+    if (tile == kTile256x128) return conv_go<bf16_t, 256, 128>(a, s);
+    return conv_go<bf16_t, 128, 128>(a, s);
+  }
+  if (tile == kTile32x256) return conv_go<float, 32, 256>(a, s);
+  return conv_go<float, 128, 128>(a, s);
+}
+
+hipError_t launch_norm(const NormArgs& a, int dtype, hipStream_t s) {
+  const int64_t M = (int64_t)a.F * a.B * a.HW;
+  const unsigned blocks = (unsigned)((M + 3) / 4);
+  if (dtype == kBF16)
+    hipLaunchKernelGGL(k_norm<bf16_t>, dim3(blocks), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_norm<float>, dim3(blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename T, int NW, int DW>
+static hipError_t attn_go(const AttnArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((k_attn<T, NW, DW>), dim3((unsigned)((a.S + 31) / 32), (unsigned)a.nfr), dim3(64 * NW), 0, s, a);
+  return hipGetLastError();
+}
+
+bool attn_supported(int C, int dtype) {
+  (void)dtype;
+  return C == 64 || C == 128 || C == 256 || C == 512 || C == 1024;
+}
+
+hipError_t launch_attn(const AttnArgs& a, int dtype, hipStream_t s) {
+  if (dtype == kBF16) {
+    switch (a.C) {
+      case 64: return attn_go<bf16_t, 2, 32>(a, s);
+      case 128: return attn_go<bf16_t, 4, 32>(a, s);
+      case 256: return attn_go<bf16_t, 4, 64>(a, s);
+      case 512: return attn_go<bf16_t, 4, 128>(a, s);
+      case 1024: return attn_go<bf16_t, 4, 256>(a, s);
+    }
+  } else {
+    switch (a.C) {
+      case 64: return attn_go<float, 4, 16>(a, s);
+      case 128: return attn_go<float, 8, 16>(a, s);
+      case 256: return attn_go<float, 8, 32>(a, s);
+      case 512: return attn_go<float, 8, 64>(a, s);
+      case 1024: return attn_go<float, 8, 128>(a, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_repack(const void* w, int src_dtype, void* dst, int dst_dtype, int Cout, int Cin, int taps,
+                         hipStream_t s) {
+  const int g = grid_for((int64_t)Cout * Cin * taps, 256);
+  if (src_dtype == kF32 && dst_dtype == kF32)
+    hipLaunchKernelGGL((k_repack<float, float>), dim3(g), dim3(256), 0, s, (const float*)w, (float*)dst, Cout, Cin, taps);
+  else if (src_dtype == kF32)
+    hipLaunchKernelGGL((k_repack<float, bf16_t>), dim3(g), dim3(256), 0, s, (const float*)w, (bf16_t*)dst, Cout, Cin, taps);
+  else if (dst_dtype == kF32)
+    hipLaunchKernelGGL((k_repack<bf16_t, float>), dim3(g), dim3(256), 0, s, (const bf16_t*)w, (float*)dst, Cout, Cin, taps);
+  else
+    hipLaunchKernelGGL((k_repack<bf16_t, bf16_t>), dim3(g), dim3(256), 0, s, (const bf16_t*)w, (bf16_t*)dst, Cout, Cin, taps);
+  return hipGetLastError();
+}
+
+hipError_t launch_to_f32(const void* x, int src_dtype, float* dst, int64_t n, int dtype, hipStream_t s) {
+  const int g = grid_for(n, 256);
+  if (src_dtype == kF32)
+    hipLaunchKernelGGL(k_to_f32<float>, dim3(g), dim3(256), 0, s, (const float*)x, dst, n, dtype == kBF16 ? 1 : 0);
+  else
+    hipLaunchKernelGGL(k_to_f32<bf16_t>, dim3(g), dim3(256), 0, s, (const bf16_t*)x, dst, n, dtype == kBF16 ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_ncthw_to_frames(const void* x, int src_dtype, void* dst, int dst_dtype, int B, int C, int Cp, int T,
+                                  int H, int W, hipStream_t s) {
+  const int g = grid_for((int64_t)T * B * H * W * Cp, 256);
+  if (src_dtype == kF32 && dst_dtype == kF32)
+    hipLaunchKernelGGL((k_ncthw_to_frames<float, float>), dim3(g), dim3(256), 0, s, (const float*)x, (float*)dst, B, C, Cp, T, H, W);
+  else if (src_dtype == kF32)
+    hipLaunchKernelGGL((k_ncthw_to_frames<float, bf16_t>), dim3(g), dim3(256), 0, s, (const float*)x, (bf16_t*)dst, B, C, Cp, T, H, W);
+  else if (dst_dtype == kF32)
+    hipLaunchKernelGGL((k_ncthw_to_frames<bf16_t, float>), dim3(g), dim3(256), 0, s, (const bf16_t*)x, (float*)dst, B, C, Cp, T, H, W);
+  else
+    hipLaunchKernelGGL((k_ncthw_to_frames<bf16_t, bf16_t>), dim3(g), dim3(256), 0, s, (const bf16_t*)x, (bf16_t*)dst, B, C, Cp, T, H, W);
+  return hipGetLastError();
+}
+
+hipError_t launch_frames_to_ncthw(const void* x, void* dst, int dtype, int B, int C, int T, int H, int W,
+                                  hipStream_t s) {
+  const int g = grid_for((int64_t)B * C * T * H * W, 256);
+  if (dtype == kF32)
+    hipLaunchKernelGGL(k_frames_to_ncthw<float>, dim3(g), dim3(256), 0, s, (const float*)x, (float*)dst, B, C, T, H, W);
+  else
+    hipLaunchKernelGGL(k_frames_to_ncthw<bf16_t>, dim3(g), dim3(256), 0, s, (const bf16_t*)x, (bf16_t*)dst, B, C, T, H, W);
+  return hipGetLastError();
+}
+
+}  // namespace wanvae

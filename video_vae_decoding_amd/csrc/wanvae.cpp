@@ -1,0 +1,985 @@
+// Host side of the MI355X Wan2.2 TI2V-5B VAE decoder: the C ABI of include/wanvae.h,
+// argument validation (done before anything is launched), topology inference from the
+// parameter shapes, the workspace plan, and the chunk loop that enqueues the kernels.
+//
+// What is computed follows FastVideo's "wan22_vae_decode reference.py" page: post_quant_conv
+// over all latent frames, then one latent frame per chunk through conv_in, the mid block
+// (residual block, attention, residual block), up blocks 0-3, norm_out + SiLU and conv_out,
+// the chunks' frames written straight into the video (unpatchified and clamped).
+//
+// Causal caches ("Causal caches" section): every conv with a 3-frame kernel owns a ring
+// of frames in the workspace. The producer of the conv's input (a norm pass or a conv
+// epilogue) writes the chunk's frames into the ring's next slots; the conv reads its last
+// <= 2 frames (history) and the new ones through a frame-pointer table, zeros standing in
+// for missing history. No cache is ever copied or concatenated.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "internal.h"
+#include "wanvae.h"
+
+namespace wanvae {
+
+static thread_local std::string g_err;
+
+static int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define HIP_TRY(expr)                                                                         \
+  do {                                                                                        \
+    hipError_t e_ = (expr);                                                                   \
+    if (e_ != hipSuccess) return fail(WANVAE_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+static size_t esize(int dtype) { return dtype == kBF16 ? 2 : 4; }
+
+// ------------------------------------------------------------------ kernel timing
+
+struct ProfRec {
+  hipEvent_t a, b;
+  int kind;
+  double flops, bytes;
+};
+
+struct Profiler {
+  bool on = false;
+  std::vector<ProfRec> recs;
+  std::vector<hipEvent_t> pool;
+  hipEvent_t event() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+  void clear() {
+    for (auto& r : recs) {
+      pool.push_back(r.a);
+      pool.push_back(r.b);
+    }
+    recs.clear();
+  }
+};
+
+static thread_local Profiler g_prof;
+
+// Starts timing a launch on st (a no-op unless timing is enabled).
+static hipEvent_t prof_start(hipStream_t st) {
+  if (!g_prof.on) return nullptr;
+  hipEvent_t a = g_prof.event();
+  if (a && hipEventRecord(a, st) != hipSuccess) return nullptr;
+  return a;
+}
+
+static void prof_stop(hipEvent_t a, int kind, double flops, double bytes, hipStream_t st) {
+  if (!a) return;
+  hipEvent_t b = g_prof.event();
+  if (!b || hipEventRecord(b, st) != hipSuccess) return;
+  g_prof.recs.push_back({a, b, kind, flops, bytes});
+}
+static int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+// ------------------------------------------------------------------ workspace planning
+
+// Bump allocator: with base == nullptr it only measures.
+struct Arena {
+  char* base = nullptr;
+  size_t used = 0;
+  void* take(size_t bytes) {
+    size_t off = align_up((int64_t)used, 256);
+    used = off + align_up((int64_t)bytes, 256);
+    return base ? base + off : nullptr;
+  }
+};
+
+// A frame table: n frames, each [B][H][W][C] at f[i] (nullptr = zero frame), batch stride bs elements.
+struct FrameRef {
+  void* f[kMaxFrames] = {};
+  int64_t bs[kMaxFrames] = {};
+  int n = 0;
+  void push(void* p, int64_t s) {
+    f[n] = p;
+    bs[n++] = s;
+  }
+};
+
+static FrameRef frames_of(void* base, int F, int64_t frame_elems, int64_t bs, size_t es) {
+  FrameRef r;
+  for (int t = 0; t < F; ++t) r.push(base ? (char*)base + (int64_t)t * frame_elems * es : nullptr, bs);
+  return r;
+}
+
+// Ring of frames holding a causal conv's input: history and the current chunk.
+struct Ring {
+  char* base = nullptr;
+  int64_t fbytes = 0, bs = 0;
+  int R = 0, head = 0, count = 0;
+  void* slot(int k) const { return base + (int64_t)(((k % R) + R) % R) * fbytes; }
+  FrameRef write(int F) const {
+    FrameRef r;
+    for (int t = 0; t < F; ++t) r.push(slot(head + t), bs);
+    return r;
+  }
+  // the conv's time-padded input: 2 - hist zero frames, hist history frames, F new frames
+  FrameRef read(int F) const {
+    FrameRef r;
+    const int hist = std::min(count, 2);
+    for (int z = 0; z < 2 - hist; ++z) r.push(nullptr, bs);
+    for (int k = 0; k < hist; ++k) r.push(slot(head - hist + k), bs);
+    for (int t = 0; t < F; ++t) r.push(slot(head + t), bs);
+    return r;
+  }
+  void commit(int F) {
+    head = (head + F) % R;
+    count += F;
+  }
+};
+
+// ------------------------------------------------------------------ parameters and topology
+
+struct ConvSpec {
+  std::string name;
+  int Cout, Cin, kt, kh, kw;
+  bool conv2d;  // [Co, Ci, kh, kw]
+};
+
+struct Topology {
+  int base = 0, c4 = 0, c2 = 0, c1 = 0, z = 48;
+  std::vector<ConvSpec> convs;
+  std::vector<std::pair<std::string, int>> norms;  // gamma name, C
+};
+
+struct UpSpec {
+  int cin, cout;
+  bool temporal, spatial;
+};
+
+static void up_specs(int base, UpSpec u[4]) {
+  u[0] = {4 * base, 4 * base, true, true};
+  u[1] = {4 * base, 4 * base, true, true};
+  u[2] = {4 * base, 2 * base, false, true};
+  u[3] = {2 * base, base, false, false};
+}
+
+static void make_topology(int base, Topology& tp) {
+  tp.base = base;
+  tp.c4 = 4 * base;
+  tp.c2 = 2 * base;
+  tp.c1 = base;
+  auto conv = [&](const std::string& n, int co, int ci, int kt, int kh, int kw, bool c2d = false) {
+    tp.convs.push_back({n, co, ci, kt, kh, kw, c2d});
+  };
+  auto resnet = [&](const std::string& p, int ci, int co) {
+    tp.norms.push_back({p + ".norm1.gamma", ci});
+    conv(p + ".conv1", co, ci, 3, 3, 3);
+    tp.norms.push_back({p + ".norm2.gamma", co});
+    conv(p + ".conv2", co, co, 3, 3, 3);
+    if (ci != co) conv(p + ".conv_shortcut", co, ci, 1, 1, 1);
+  };
+  const int c = tp.c4;
+  conv("post_quant_conv", tp.z, tp.z, 1, 1, 1);
+  conv("decoder.conv_in", c, tp.z, 3, 3, 3);
+  resnet("decoder.mid_block.resnets.0", c, c);
+  tp.norms.push_back({"decoder.mid_block.attentions.0.norm.gamma", c});
+  conv("decoder.mid_block.attentions.0.to_qkv", 3 * c, c, 1, 1, 1, true);
+  conv("decoder.mid_block.attentions.0.proj", c, c, 1, 1, 1, true);
+  resnet("decoder.mid_block.resnets.1", c, c);
+  UpSpec u[4];
+  up_specs(base, u);
+  for (int i = 0; i < 4; ++i) {
+    const std::string p = "decoder.up_blocks." + std::to_string(i);
+    for (int j = 0; j < 3; ++j) resnet(p + ".resnets." + std::to_string(j), j == 0 ? u[i].cin : u[i].cout, u[i].cout);
+    if (u[i].temporal) conv(p + ".upsampler.time_conv", 2 * u[i].cout, u[i].cout, 3, 1, 1);
+    if (u[i].spatial) conv(p + ".upsampler.resample.1", u[i].cout, u[i].cout, 1, 3, 3, true);
+  }
+  tp.norms.push_back({"decoder.norm_out.gamma", base});
+  conv("decoder.conv_out", 12, base, 3, 3, 3);
+}
+
+using WeightMap = std::unordered_map<std::string, const wanvae_tensor*>;
+
+static bool has_prefix(const char* s, const char* p) { return strncmp(s, p, strlen(p)) == 0; }
+
+static int64_t numel(const wanvae_tensor* t) {
+  int64_t n = 1;
+  for (int i = 0; i < t->ndim; ++i) n *= t->shape[i];
+  return n;
+}
+
+static int check_tensor(const wanvae_tensor* t, const char* what) {
+  if (!t) return fail(WANVAE_EARG, "%s: NULL tensor", what);
+  if (t->dtype != kF32 && t->dtype != kBF16)
+    return fail(WANVAE_EDTYPE, "%s: element type %d is neither WANVAE_F32 nor WANVAE_BF16", what, t->dtype);
+  if (t->ndim < 0 || t->ndim > 5) return fail(WANVAE_ESHAPE, "%s: ndim %d not in [0, 5]", what, t->ndim);
+  if (!t->data) return fail(WANVAE_EARG, "%s: NULL data pointer", what);
+  for (int i = 0; i < t->ndim; ++i)
+    if (t->shape[i] < 0) return fail(WANVAE_ESHAPE, "%s: negative extent", what);
+  return WANVAE_OK;
+}
+
+static int parse_weights(const wanvae_tensor* ws, int64_t n, WeightMap& m) {
+  if (n < 0 || (n > 0 && !ws)) return fail(WANVAE_EARG, "weights: NULL table or negative count");
+  for (int64_t i = 0; i < n; ++i) {
+    const wanvae_tensor* t = ws + i;
+    if (!t->name) return fail(WANVAE_EARG, "weights[%lld]: NULL name", (long long)i);
+    if (!has_prefix(t->name, "decoder.") && !has_prefix(t->name, "post_quant_conv.")) continue;
+    if (!m.emplace(t->name, t).second) return fail(WANVAE_EARG, "duplicate parameter name %s", t->name);
+    if (int rc = check_tensor(t, t->name)) return rc;
+  }
+  return WANVAE_OK;
+}
+
+static bool shape_is(const wanvae_tensor* t, std::initializer_list<int64_t> s) {
+  if (t->ndim != (int)s.size()) return false;
+  int i = 0;
+  for (int64_t v : s)
+    if (t->shape[i++] != v) return false;
+  return true;
+}
+
+static std::string shape_str(const wanvae_tensor* t) {
+  std::string s = "[";
+  for (int i = 0; i < t->ndim; ++i) s += (i ? "," : "") + std::to_string(t->shape[i]);
+  return s + "]";
+}
+
+static int build_topology(const WeightMap& m, Topology& tp) {
+  auto it = m.find("decoder.conv_out.weight");
+  if (it == m.end()) return fail(WANVAE_EMISSING, "missing parameter decoder.conv_out.weight");
+  if (it->second->ndim != 5) return fail(WANVAE_ESHAPE, "decoder.conv_out.weight: shape %s", shape_str(it->second).c_str());
+  const int64_t base = it->second->shape[1];
+  auto pq = m.find("post_quant_conv.weight");
+  if (pq == m.end()) return fail(WANVAE_EMISSING, "missing parameter post_quant_conv.weight");
+  if (pq->second->ndim != 5 || pq->second->shape[0] != 48)
+    return fail(WANVAE_ETOPOLOGY, "post_quant_conv.weight %s: the decoder needs z_dim 48", shape_str(pq->second).c_str());
+  if (base < 16 || base % 16 != 0 || 4 * base > 1024)
+    return fail(WANVAE_ETOPOLOGY, "decoder_base_dim %lld unsupported (needs a multiple of 16, at most 256)", (long long)base);
+  make_topology((int)base, tp);
+  for (const ConvSpec& c : tp.convs) {
+    const std::string wn = c.name + ".weight", bn = c.name + ".bias";
+    auto w = m.find(wn);
+    if (w == m.end()) return fail(WANVAE_EMISSING, "missing parameter %s", wn.c_str());
+    auto b = m.find(bn);
+    if (b == m.end()) return fail(WANVAE_EMISSING, "missing parameter %s", bn.c_str());
+    bool ok;
+    if (c.conv2d)
+      ok = shape_is(w->second, {c.Cout, c.Cin, c.kh, c.kw}) ||
+           (c.kh == 1 && shape_is(w->second, {c.Cout, c.Cin}));
+    else
+      ok = shape_is(w->second, {c.Cout, c.Cin, c.kt, c.kh, c.kw});
+    if (!ok) return fail(WANVAE_ESHAPE, "%s: shape %s does not fit the decoder", wn.c_str(), shape_str(w->second).c_str());
+    if (!shape_is(b->second, {c.Cout}))
+      return fail(WANVAE_ESHAPE, "%s: shape %s, expected [%d]", bn.c_str(), shape_str(b->second).c_str(), c.Cout);
+  }
+  for (auto& g : tp.norms) {
+    auto w = m.find(g.first);
+    if (w == m.end()) return fail(WANVAE_EMISSING, "missing parameter %s", g.first.c_str());
+    if (numel(w->second) != g.second)
+      return fail(WANVAE_ESHAPE, "%s: %lld elements, expected %d", g.first.c_str(), (long long)numel(w->second), g.second);
+  }
+  return WANVAE_OK;
+}
+
+// ------------------------------------------------------------------ launch helpers
+
+struct ConvW {
+  void* w = nullptr;
+  float* b = nullptr;
+  int Cout = 0, Cin = 0, kt = 1, kh = 1, kw = 1;
+};
+
+static int prep_conv(Arena& ar, int dtype, const wanvae_tensor* w, const wanvae_tensor* b, int Cout, int Cin, int kt,
+                     int kh, int kw, ConvW& out, hipStream_t st) {
+  out.Cout = Cout, out.Cin = Cin, out.kt = kt, out.kh = kh, out.kw = kw;
+  const int taps = kt * kh * kw;
+  out.w = ar.take((size_t)Cout * taps * Cin * esize(dtype));
+  out.b = (float*)ar.take((size_t)Cout * 4);
+  if (!ar.base) return WANVAE_OK;
+  hipEvent_t e0 = prof_start(st);
+  HIP_TRY(launch_repack(w->data, w->dtype, out.w, dtype, Cout, Cin, taps, st));
+  HIP_TRY(launch_to_f32(b->data, b->dtype, out.b, Cout, dtype, st));
+  prof_stop(e0, WANVAE_KOTHER, 0, (double)Cout * taps * Cin * (esize(w->dtype) + esize(dtype)), st);
+  return WANVAE_OK;
+}
+
+static int prep_vec(Arena& ar, int dtype, const wanvae_tensor* g, int C, float*& out, hipStream_t st) {
+  out = (float*)ar.take((size_t)C * 4);
+  if (!ar.base) return WANVAE_OK;
+  HIP_TRY(launch_to_f32(g->data, g->dtype, out, C, dtype, st));
+  return WANVAE_OK;
+}
+
+struct ConvCall {
+  ConvArgs a;
+  ConvCall() { memset(&a, 0, sizeof a); }
+};
+
+static int run_conv(const ConvW& cw, const FrameRef& in, int B, int Hin, int Win, int Ho, int Wo, int F, bool up,
+                    ConvCall& cc, int dtype, hipStream_t st) {
+  ConvArgs& a = cc.a;
+  if (in.n != F + cw.kt - 1 || in.n > kMaxFrames)
+    return fail(WANVAE_EARG, "internal: conv frame table has %d frames for %d outputs", in.n, F);
+  for (int i = 0; i < in.n; ++i) {
+    a.in[i] = in.f[i];
+    a.in_bs[i] = in.bs[i];
+  }
+  a.B = B, a.Hin = Hin, a.Win = Win, a.Cin = cw.Cin;
+  a.Ho = Ho, a.Wo = Wo, a.Cout = cw.Cout;
+  a.kt = cw.kt, a.kh = cw.kh, a.kw = cw.kw;
+  a.up = up ? 1 : 0;
+  a.F = F;
+  a.w = cw.w;
+  a.bias = cw.b;
+  const int tile = cw.Cout <= 64 ? kTile32x256 : kTile128x128;
+  // algorithmic FLOPs: every output, every spatial tap, the time taps on real frames
+  double taps_real = 0;
+  for (int t = 0; t < F; ++t)
+    for (int dt = 0; dt < cw.kt; ++dt) taps_real += in.f[t + dt] ? 1 : 0;
+  const double flops = 2.0 * B * Ho * Wo * (double)cw.Cout * cw.Cin * cw.kh * cw.kw * taps_real;
+  hipEvent_t e0 = prof_start(st);
+  HIP_TRY(launch_conv(a, dtype, tile, st));
+  prof_stop(e0, WANVAE_KCONV, flops, 0, st);
+  return WANVAE_OK;
+}
+
+static void set_out(ConvArgs& a, const FrameRef& o, int outC) {
+  for (int i = 0; i < o.n; ++i) {
+    a.out[i] = o.f[i];
+    a.out_bs[i] = o.bs[i];
+  }
+  a.outC = outC;
+}
+
+static void set_res(ConvArgs& a, const FrameRef& r) {
+  a.has_res = 1;
+  for (int i = 0; i < r.n; ++i) {
+    a.res[i] = r.f[i];
+    a.res_bs[i] = r.bs[i];
+  }
+}
+
+static int run_norm(const FrameRef& in, const FrameRef& out, int F, int B, int HW, int C, const float* gamma, bool silu,
+                    int dtype, hipStream_t st) {
+  NormArgs n;
+  memset(&n, 0, sizeof n);
+  if (in.n < F || out.n < F) return fail(WANVAE_EARG, "internal: norm frame tables too short");
+  for (int t = 0; t < F; ++t) {
+    n.in[t] = in.f[t];
+    n.in_bs[t] = in.bs[t];
+    n.out[t] = out.f[t];
+    n.out_bs[t] = out.bs[t];
+  }
+  n.F = F, n.B = B, n.HW = HW, n.C = C;
+  n.gamma = gamma;
+  n.sqrtC = (float)std::sqrt((double)C);
+  n.silu = silu ? 1 : 0;
+  hipEvent_t e0 = prof_start(st);
+  HIP_TRY(launch_norm(n, dtype, st));
+  prof_stop(e0, WANVAE_KNORM, 0, 2.0 * F * B * (double)HW * C * esize(dtype), st);
+  return WANVAE_OK;
+}
+
+// Attention block on nfr independent frames folded into the batch (F = 1, B = nfr):
+// n = RMS norm (no SiLU) -> 1x1 conv to q, k, v^T -> flash attention -> 1x1 proj + x.
+struct AttnBufs {
+  void *n = nullptr, *q = nullptr, *k = nullptr, *vt = nullptr, *o = nullptr;
+  int S = 0, Sp = 0;
+};
+
+static void plan_attn_bufs(Arena& ar, AttnBufs& ab, int nfr, int S, int C, int dtype) {
+  const size_t es = esize(dtype);
+  ab.S = S;
+  ab.Sp = (int)align_up(S, 32);
+  ab.n = ar.take((size_t)nfr * S * C * es);
+  ab.q = ar.take((size_t)nfr * S * C * es);
+  ab.k = ar.take((size_t)nfr * S * C * es);
+  ab.vt = ar.take((size_t)nfr * C * ab.Sp * es);
+  ab.o = ar.take((size_t)nfr * S * C * es);
+}
+
+static int run_attn(const FrameRef& x, const FrameRef& y, int nfr, int H, int W, int C, const float* gamma,
+                    const ConvW& qkv, const ConvW& proj, const AttnBufs& ab, int dtype, hipStream_t st) {
+  const size_t es = esize(dtype);
+  const int S = H * W;
+  const FrameRef n = frames_of(ab.n, 1, (int64_t)nfr * S * C, (int64_t)S * C, es);
+  if (int rc = run_norm(x, n, 1, nfr, S, C, gamma, false, dtype, st)) return rc;
+  HIP_TRY(hipMemsetAsync(ab.vt, 0, (size_t)nfr * C * ab.Sp * es, st));
+  {
+    ConvCall cc;
+    cc.a.mode = kEpiQKV;
+    cc.a.outC = C;
+    cc.a.q = ab.q, cc.a.k = ab.k, cc.a.vt = ab.vt;
+    cc.a.S = S, cc.a.Sp = ab.Sp;
+    if (int rc = run_conv(qkv, n, nfr, H, W, H, W, 1, false, cc, dtype, st)) return rc;
+  }
+  AttnArgs aa;
+  aa.q = ab.q, aa.k = ab.k, aa.vt = ab.vt, aa.o = ab.o;
+  aa.nfr = nfr, aa.S = S, aa.Sp = ab.Sp, aa.C = C;
+  aa.scale = (float)(1.0 / std::sqrt((double)C));
+  hipEvent_t e0 = prof_start(st);
+  HIP_TRY(launch_attn(aa, dtype, st));
+  prof_stop(e0, WANVAE_KATTN, 4.0 * nfr * (double)S * S * C, 0, st);
+  {
+    ConvCall cc;
+    cc.a.mode = kEpiFrames;
+    set_out(cc.a, y, C);
+    set_res(cc.a, x);
+    const FrameRef o = frames_of(ab.o, 1, (int64_t)nfr * S * C, (int64_t)S * C, es);
+    if (int rc = run_conv(proj, o, nfr, H, W, H, W, 1, false, cc, dtype, st)) return rc;
+  }
+  return WANVAE_OK;
+}
+
+// ------------------------------------------------------------------ the decoder
+
+struct Level {
+  int H = 0, W = 0, F = 0, C = 0;  // resolution, max frames per chunk, max channels
+  void* x[3] = {};
+  void* h = nullptr;
+  void* s = nullptr;
+  void* tb = nullptr;  // time conv output (2F frames), up blocks 0 and 1
+};
+
+class Decoder {
+ public:
+  Decoder(const WeightMap& m, const Topology& tp, int dtype, int B, int T, int h, int w)
+      : m_(m), tp_(tp), dt_(dtype), es_(esize(dtype)), B_(B), T_(T), h_(h), w_(w) {}
+
+  // Lays out the workspace (measuring when ar.base is null) and, with a real base, enqueues
+  // the weight preparation.
+  int plan(Arena& ar, hipStream_t st) {
+    st_ = st;
+    for (const ConvSpec& c : tp_.convs) {
+      ConvW& cw = cw_[c.name];
+      if (int rc = prep_conv(ar, dt_, m_.at(c.name + ".weight"), m_.at(c.name + ".bias"), c.Cout, c.Cin, c.kt, c.kh,
+                             c.kw, cw, st))
+        return rc;
+    }
+    for (auto& g : tp_.norms)
+      if (int rc = prep_vec(ar, dt_, m_.at(g.first), g.second, gam_[g.first], st)) return rc;
+    const int c4 = tp_.c4, c2 = tp_.c2, c1 = tp_.c1;
+    const int fmax[4] = {1, T_ > 1 ? 2 : 1, T_ > 1 ? 4 : 1, T_ > 1 ? 4 : 1};
+    const int cmax[4] = {c4, c4, c4, c2};
+    for (int l = 0; l < 4; ++l) {
+      Level& L = lv_[l];
+      L.H = h_ << l, L.W = w_ << l, L.F = fmax[l], L.C = cmax[l];
+      const size_t bytes = (size_t)L.F * B_ * L.H * L.W * L.C * es_;
+      for (int i = 0; i < 3; ++i) L.x[i] = ar.take(bytes);
+      L.h = ar.take(bytes);
+      if (l >= 2) L.s = ar.take(bytes);
+      if (l <= 1) L.tb = ar.take(2 * bytes);
+    }
+    zt_ = ar.take((size_t)T_ * B_ * h_ * w_ * tp_.z * es_);
+    pq_ = ar.take((size_t)T_ * B_ * h_ * w_ * tp_.z * es_);
+    // rings of the 3-frame convs: conv1/conv2 of every residual block, the time convs, conv_out
+    auto ring = [&](const std::string& name, int l, int C) {
+      Ring& r = rings_[name];
+      const Level& L = lv_[l];
+      r.R = L.F + 2;
+      r.fbytes = (int64_t)B_ * L.H * L.W * C * es_;
+      r.bs = (int64_t)L.H * L.W * C;
+      r.base = (char*)ar.take((size_t)r.R * r.fbytes);
+    };
+    auto resnet_rings = [&](const std::string& p, int l, int ci, int co) {
+      ring(p + ".conv1", l, ci);
+      ring(p + ".conv2", l, co);
+    };
+    resnet_rings("decoder.mid_block.resnets.0", 0, c4, c4);
+    resnet_rings("decoder.mid_block.resnets.1", 0, c4, c4);
+    UpSpec u[4];
+    up_specs(tp_.base, u);
+    for (int i = 0; i < 4; ++i) {
+      const std::string p = "decoder.up_blocks." + std::to_string(i);
+      for (int j = 0; j < 3; ++j) resnet_rings(p + ".resnets." + std::to_string(j), i, j == 0 ? u[i].cin : u[i].cout, u[i].cout);
+      if (u[i].temporal) ring(p + ".upsampler.time_conv", i, u[i].cout);
+    }
+    ring("decoder.conv_out", 3, c1);
+    plan_attn_bufs(ar, ab_, B_, h_ * w_, c4, dt_);
+    return WANVAE_OK;
+  }
+
+  int run(const void* z, int z_dtype, void* video) {
+    const int64_t zf = (int64_t)B_ * h_ * w_ * tp_.z;
+    HIP_TRY(launch_ncthw_to_frames(z, z_dtype, zt_, dt_, B_, tp_.z, tp_.z, T_, h_, w_, st_));
+    {  // post_quant_conv over all T latent frames at once (frames folded into the batch)
+      ConvCall cc;
+      cc.a.mode = kEpiFrames;
+      set_out(cc.a, frames_of(pq_, 1, 0, (int64_t)h_ * w_ * tp_.z, es_), tp_.z);
+      const FrameRef in = frames_of(zt_, 1, 0, (int64_t)h_ * w_ * tp_.z, es_);
+      if (int rc = run_conv(cw_.at("post_quant_conv"), in, T_ * B_, h_, w_, h_, w_, 1, false, cc, dt_, st_)) return rc;
+    }
+    for (int i = 0; i < T_; ++i)
+      if (int rc = chunk(i, video)) return rc;
+    (void)zf;
+    return WANVAE_OK;
+  }
+
+ private:
+  FrameRef lvl_frames(int l, void* base, int F, int C) const {
+    const Level& L = lv_[l];
+    return frames_of(base, F, (int64_t)B_ * L.H * L.W * C, (int64_t)L.H * L.W * C, es_);
+  }
+
+  int conv_into(const std::string& name, const FrameRef& in, int l, int F, const FrameRef& out,
+                const FrameRef* res) {
+    const ConvW& cw = cw_.at(name);
+    const Level& L = lv_[l];
+    ConvCall cc;
+    cc.a.mode = kEpiFrames;
+    set_out(cc.a, out, cw.Cout);
+    if (res) set_res(cc.a, *res);
+    return run_conv(cw, in, B_, L.H, L.W, L.H, L.W, F, false, cc, dt_, st_);
+  }
+
+  // WanResidualBlock: x2 + shortcut with x1 = conv1(SiLU(norm1(x))), x2 = conv2(SiLU(norm2(x1)))
+  int resnet(const std::string& p, int l, int F, const FrameRef& x, int ci, int co, const FrameRef& out) {
+    const Level& L = lv_[l];
+    const int HW = L.H * L.W;
+    FrameRef res = x;
+    if (ci != co) {
+      res = lvl_frames(l, L.s, F, co);
+      if (int rc = conv_into(p + ".conv_shortcut", x, l, F, res, nullptr)) return rc;
+    }
+    Ring& r1 = rings_.at(p + ".conv1");
+    if (int rc = run_norm(x, r1.write(F), F, B_, HW, ci, gam_.at(p + ".norm1.gamma"), true, dt_, st_)) return rc;
+    const FrameRef hbuf = lvl_frames(l, L.h, F, co);
+    if (int rc = conv_into(p + ".conv1", r1.read(F), l, F, hbuf, nullptr)) return rc;
+    r1.commit(F);
+    Ring& r2 = rings_.at(p + ".conv2");
+    if (int rc = run_norm(hbuf, r2.write(F), F, B_, HW, co, gam_.at(p + ".norm2.gamma"), true, dt_, st_)) return rc;
+    if (int rc = conv_into(p + ".conv2", r2.read(F), l, F, out, &res)) return rc;
+    r2.commit(F);
+    return WANVAE_OK;
+  }
+
+  int chunk(int i, void* video) {
+    const bool first = i == 0;
+    const int c4 = tp_.c4;
+    // conv_in: latent frames i-2, i-1 (history) and i, read in place from the post_quant output
+    {
+      FrameRef in;
+      const int64_t fe = (int64_t)B_ * h_ * w_ * tp_.z;
+      for (int s = i - 2; s <= i; ++s) in.push(s < 0 ? nullptr : (char*)pq_ + s * fe * es_, (int64_t)h_ * w_ * tp_.z);
+      if (int rc = conv_into("decoder.conv_in", in, 0, 1, lvl_frames(0, lv_[0].x[0], 1, c4), nullptr)) return rc;
+    }
+    Level& L0 = lv_[0];
+    const FrameRef x0 = lvl_frames(0, L0.x[0], 1, c4), x1 = lvl_frames(0, L0.x[1], 1, c4),
+                   x2 = lvl_frames(0, L0.x[2], 1, c4);
+    if (int rc = resnet("decoder.mid_block.resnets.0", 0, 1, x0, c4, c4, x1)) return rc;
+    {
+      const std::string a = "decoder.mid_block.attentions.0";
+      if (int rc = run_attn(x1, x2, B_, h_, w_, c4, gam_.at(a + ".norm.gamma"), cw_.at(a + ".to_qkv"),
+                            cw_.at(a + ".proj"), ab_, dt_, st_))
+        return rc;
+    }
+    if (int rc = resnet("decoder.mid_block.resnets.1", 0, 1, x2, c4, c4, x0)) return rc;
+
+    UpSpec u[4];
+    up_specs(tp_.base, u);
+    int F = 1;
+    for (int b = 0; b < 4; ++b) {
+      Level& L = lv_[b];
+      const std::string p = "decoder.up_blocks." + std::to_string(b);
+      const FrameRef xin = lvl_frames(b, L.x[0], F, u[b].cin);
+      const FrameRef xa = lvl_frames(b, L.x[1], F, u[b].cout), xb = lvl_frames(b, L.x[2], F, u[b].cout);
+      if (int rc = resnet(p + ".resnets.0", b, F, xin, u[b].cin, u[b].cout, xa)) return rc;
+      if (int rc = resnet(p + ".resnets.1", b, F, xa, u[b].cout, u[b].cout, xb)) return rc;
+      const bool tconv = u[b].temporal && !first;
+      Ring* tr = tconv ? &rings_.at(p + ".upsampler.time_conv") : nullptr;
+      const FrameRef r2out = tconv ? tr->write(F) : xa;
+      if (int rc = resnet(p + ".resnets.2", b, F, xb, u[b].cout, u[b].cout, r2out)) return rc;
+      if (!u[b].spatial) {
+        // norm_out + SiLU -> conv_out -> unpatchify + clamp straight into the video
+        Ring& ro = rings_.at("decoder.conv_out");
+        if (int rc = run_norm(r2out, ro.write(F), F, B_, L.H * L.W, u[b].cout, gam_.at("decoder.norm_out.gamma"), true,
+                              dt_, st_))
+          return rc;
+        const ConvW& cw = cw_.at("decoder.conv_out");
+        ConvCall cc;
+        cc.a.mode = kEpiVideo;
+        cc.a.video = video;
+        cc.a.vF = 4 * T_ - 3;
+        cc.a.vf0 = first ? 0 : 4 * i - 3;
+        if (int rc = run_conv(cw, ro.read(F), B_, L.H, L.W, L.H, L.W, F, false, cc, dt_, st_)) return rc;
+        ro.commit(F);
+        break;
+      }
+      FrameRef src = r2out;
+      int Fs = F;
+      if (tconv) {
+        // upsample3d's time conv: C -> 2C, channel c -> frame 2t, channel C + c -> frame 2t + 1
+        const ConvW& cw = cw_.at(p + ".upsampler.time_conv");
+        ConvCall cc;
+        cc.a.mode = kEpiInterleave;
+        src = lvl_frames(b, L.tb, 2 * F, u[b].cout);
+        set_out(cc.a, src, u[b].cout);
+        if (int rc = run_conv(cw, tr->read(F), B_, L.H, L.W, L.H, L.W, F, false, cc, dt_, st_)) return rc;
+        tr->commit(F);
+        Fs = 2 * F;
+      }
+      // upsample2d (nearest x2 read through the conv's addressing, 3x3 conv) + DupUp3D(block input)
+      Level& N = lv_[b + 1];
+      const ConvW& cw = cw_.at(p + ".upsampler.resample.1");
+      ConvCall cc;
+      cc.a.mode = kEpiFrames;
+      set_out(cc.a, lvl_frames(b + 1, N.x[0], Fs, u[b].cout), u[b].cout);
+      const int ft = u[b].temporal ? 2 : 1;
+      cc.a.has_dup = 1;
+      for (int t = 0; t < F; ++t) {
+        cc.a.dup[t] = xin.f[t];
+        cc.a.dup_bs[t] = xin.bs[t];
+      }
+      cc.a.dup_C = u[b].cin;
+      cc.a.dup_ft = ft;
+      cc.a.dup_r = u[b].cout * ft * 4 / u[b].cin;
+      cc.a.dup_shift = first ? ft - 1 : 0;
+      if (int rc = run_conv(cw, src, B_, L.H, L.W, N.H, N.W, Fs, true, cc, dt_, st_)) return rc;
+      F = Fs;
+    }
+    return WANVAE_OK;
+  }
+
+  const WeightMap& m_;
+  const Topology& tp_;
+  int dt_;
+  size_t es_;
+  int B_, T_, h_, w_;
+  hipStream_t st_ = nullptr;
+  std::unordered_map<std::string, ConvW> cw_;
+  std::unordered_map<std::string, float*> gam_;
+  std::unordered_map<std::string, Ring> rings_;
+  Level lv_[4];
+  void* zt_ = nullptr;
+  void* pq_ = nullptr;
+  AttnBufs ab_;
+};
+
+static int check_dtype(int dtype, const char* what) {
+  if (dtype != kF32 && dtype != kBF16)
+    return fail(WANVAE_EDTYPE, "%s must be WANVAE_F32 or WANVAE_BF16, not %d", what, dtype);
+  return WANVAE_OK;
+}
+
+static int decode_validate(int64_t B, int64_t T, int64_t h, int64_t w, const wanvae_tensor* weights, int64_t n,
+                           int32_t dtype, WeightMap& m, Topology& tp) {
+  if (int rc = check_dtype(dtype, "dtype")) return rc;
+  if (B < 1 || T < 1 || h < 1 || w < 1)
+    return fail(WANVAE_ESHAPE, "latent shape [%lld, 48, %lld, %lld, %lld] must have B, T, h, w >= 1", (long long)B,
+                (long long)T, (long long)h, (long long)w);
+  if (B * h * w * 64 * 64 > (int64_t)1 << 31 || T > 100000)
+    return fail(WANVAE_ESHAPE, "latent shape too large");
+  if (int rc = parse_weights(weights, n, m)) return rc;
+  return build_topology(m, tp);
+}
+
+}  // namespace wanvae
+
+using namespace wanvae;
+
+extern "C" {
+
+const char* wanvae_last_error(void) { return g_err.c_str(); }
+
+int wanvae_profile_enable(int on) {
+  g_err.clear();
+  g_prof.clear();
+  g_prof.on = on != 0;
+  return WANVAE_OK;
+}
+
+int wanvae_profile_read(int kind, double* ms, int64_t* launches, double* flops, double* bytes) {
+  g_err.clear();
+  double t = 0, f = 0, by = 0;
+  int64_t n = 0;
+  for (auto& r : g_prof.recs) {
+    if (r.kind != kind) continue;
+    HIP_TRY(hipEventSynchronize(r.b));
+    float e = 0;
+    HIP_TRY(hipEventElapsedTime(&e, r.a, r.b));
+    t += e;
+    f += r.flops;
+    by += r.bytes;
+    ++n;
+  }
+  if (ms) *ms = t;
+  if (launches) *launches = n;
+  if (flops) *flops = f;
+  if (bytes) *bytes = by;
+  return WANVAE_OK;
+}
+
+int wanvae_version(void) { return 100; }
+
+int wanvae_decode_workspace_size(int64_t B, int64_t T, int64_t h, int64_t w, const wanvae_tensor* weights,
+                                 int64_t n_weights, int32_t dtype, size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(WANVAE_EARG, "bytes: NULL");
+  WeightMap m;
+  Topology tp;
+  if (int rc = decode_validate(B, T, h, w, weights, n_weights, dtype, m, tp)) return rc;
+  Decoder d(m, tp, dtype, (int)B, (int)T, (int)h, (int)w);
+  Arena ar;
+  if (int rc = d.plan(ar, nullptr)) return rc;
+  *bytes = ar.used;
+  return WANVAE_OK;
+}
+
+int wanvae_decode(const void* z, int32_t z_dtype, int64_t B, int64_t T, int64_t h, int64_t w,
+                  const wanvae_tensor* weights, int64_t n_weights, int32_t dtype, void* video, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  WeightMap m;
+  Topology tp;
+  if (int rc = decode_validate(B, T, h, w, weights, n_weights, dtype, m, tp)) return rc;
+  if (int rc = check_dtype(z_dtype, "z_dtype")) return rc;
+  if (!z || !video) return fail(WANVAE_EARG, "z and video must not be NULL");
+  Decoder measure(m, tp, dtype, (int)B, (int)T, (int)h, (int)w);
+  Arena probe;
+  measure.plan(probe, nullptr);
+  if (workspace && workspace_bytes < probe.used)
+    return fail(WANVAE_EWORKSPACE, "workspace of %zu bytes, the decode needs %zu", workspace_bytes, probe.used);
+  hipStream_t st = (hipStream_t)stream;
+  void* ws = workspace;
+  if (!ws) HIP_TRY(hipMallocAsync(&ws, probe.used, st));
+  Decoder d(m, tp, dtype, (int)B, (int)T, (int)h, (int)w);
+  Arena ar;
+  ar.base = (char*)ws;
+  int rc = d.plan(ar, st);
+  if (rc == WANVAE_OK) rc = d.run(z, z_dtype, video);
+  if (!workspace) {
+    hipError_t e = hipFreeAsync(ws, st);
+    if (rc == WANVAE_OK && e != hipSuccess) rc = fail(WANVAE_EHIP, "hipFreeAsync: %s", hipGetErrorString(e));
+  }
+  return rc;
+}
+
+// ---------------------------------------------------------------- single causal conv
+
+static int conv_validate(const void* x, const void* cache, int64_t B, int64_t Cin, int64_t t, int64_t h, int64_t w,
+                         int64_t n_cache, const wanvae_tensor* weight, const wanvae_tensor* bias, int32_t layout,
+                         int32_t dtype, const void* y) {
+  if (int rc = check_dtype(dtype, "dtype")) return rc;
+  if (layout != WANVAE_NCTHW && layout != WANVAE_NTHWC) return fail(WANVAE_EARG, "layout %d unknown", layout);
+  if (!x || !y) return fail(WANVAE_EARG, "x and y must not be NULL");
+  if (int rc = check_tensor(weight, "weight")) return rc;
+  if (int rc = check_tensor(bias, "bias")) return rc;
+  if (B < 1 || Cin < 1 || t < 1 || h < 1 || w < 1) return fail(WANVAE_ESHAPE, "B, Cin, t, h, w must be >= 1");
+  if (Cin % 8 != 0) return fail(WANVAE_ESHAPE, "Cin %lld must be a multiple of 8", (long long)Cin);
+  if (weight->ndim != 5 || weight->shape[1] != Cin)
+    return fail(WANVAE_ESHAPE, "weight %s does not fit Cin %lld", shape_str(weight).c_str(), (long long)Cin);
+  const int64_t Cout = weight->shape[0], kt = weight->shape[2], kh = weight->shape[3], kw = weight->shape[4];
+  if (Cout < 4 || Cout % 4 != 0) return fail(WANVAE_ESHAPE, "Cout %lld must be a positive multiple of 4", (long long)Cout);
+  if ((kt != 1 && kt != 3) || (kh != 1 && kh != 3) || (kw != 1 && kw != 3))
+    return fail(WANVAE_ESHAPE, "kernel %lldx%lldx%lld: each extent must be 1 or 3", (long long)kt, (long long)kh,
+                (long long)kw);
+  if (!shape_is(bias, {Cout})) return fail(WANVAE_ESHAPE, "bias %s, expected [%lld]", shape_str(bias).c_str(), (long long)Cout);
+  if (n_cache < 0 || n_cache > 2 || (kt == 1 && n_cache != 0))
+    return fail(WANVAE_ESHAPE, "n_cache %lld (needs 0..2, and 0 for kt = 1)", (long long)n_cache);
+  if (n_cache > 0 && !cache) return fail(WANVAE_EARG, "cache NULL with n_cache %lld", (long long)n_cache);
+  if (t + kt - 1 > kMaxFrames) return fail(WANVAE_ESHAPE, "t %lld too large (at most %d)", (long long)t, kMaxFrames - 2);
+  if (B * h * w * (Cin > Cout ? Cin : Cout) > ((int64_t)1 << 31)) return fail(WANVAE_ESHAPE, "frame too large");
+  return WANVAE_OK;
+}
+
+static size_t conv_ws(int64_t B, int64_t Cin, int64_t Cout, int64_t taps, int64_t t, int64_t h, int64_t w,
+                      int64_t n_cache, int32_t layout, int32_t dtype) {
+  Arena ar;
+  ar.take((size_t)Cout * taps * Cin * esize(dtype));
+  ar.take((size_t)Cout * 4);
+  if (layout == WANVAE_NCTHW) {
+    ar.take((size_t)(t + n_cache) * B * h * w * Cin * esize(dtype));
+    ar.take((size_t)t * B * h * w * Cout * esize(dtype));
+  }
+  return ar.used;
+}
+
+int wanvae_causal_conv3d_workspace_size(int64_t B, int64_t Cin, int64_t Cout, int64_t t, int64_t h, int64_t w,
+                                        int64_t n_cache, int32_t layout, int32_t dtype, size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(WANVAE_EARG, "bytes: NULL");
+  if (int rc = check_dtype(dtype, "dtype")) return rc;
+  *bytes = conv_ws(B, Cin, Cout, 27, t, h, w, n_cache, layout, dtype);
+  return WANVAE_OK;
+}
+
+int wanvae_causal_conv3d(const void* x, const void* cache, int64_t B, int64_t Cin, int64_t t, int64_t h, int64_t w,
+                         int64_t n_cache, const wanvae_tensor* weight, const wanvae_tensor* bias, int32_t layout,
+                         int32_t dtype, void* y, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (int rc = conv_validate(x, cache, B, Cin, t, h, w, n_cache, weight, bias, layout, dtype, y)) return rc;
+  const int Cout = (int)weight->shape[0], kt = (int)weight->shape[2], kh = (int)weight->shape[3],
+            kw = (int)weight->shape[4];
+  const size_t need = conv_ws(B, Cin, Cout, kt * kh * kw, t, h, w, n_cache, layout, dtype);
+  if (workspace && workspace_bytes < need)
+    return fail(WANVAE_EWORKSPACE, "workspace of %zu bytes, the conv needs %zu", workspace_bytes, need);
+  hipStream_t st = (hipStream_t)stream;
+  void* ws = workspace;
+  if (!ws) HIP_TRY(hipMallocAsync(&ws, need, st));
+  Arena ar;
+  ar.base = (char*)ws;
+  const size_t es = esize(dtype);
+  const int64_t hw = h * w;
+  const int tpad = 2 * (kt / 2);
+  ConvW cw;
+  int rc = prep_conv(ar, dtype, weight, bias, Cout, (int)Cin, kt, kh, kw, cw, st);
+  FrameRef in, out;
+  for (int z = 0; z < tpad - n_cache; ++z) in.push(nullptr, 0);
+  void* yout = nullptr;
+  if (rc == WANVAE_OK && layout == WANVAE_NCTHW) {
+    // convert to frames [n_cache + t][B][h][w][Cin] in the workspace
+    void* xin = ar.take((size_t)(t + n_cache) * B * hw * Cin * es);
+    yout = ar.take((size_t)t * B * hw * Cout * es);
+    const int64_t fe = B * hw * Cin;
+    hipError_t e = hipSuccess;
+    if (n_cache)
+      e = launch_ncthw_to_frames(cache, dtype, xin, dtype, (int)B, (int)Cin, (int)Cin, (int)n_cache, (int)h, (int)w, st);
+    if (e == hipSuccess)
+      e = launch_ncthw_to_frames(x, dtype, (char*)xin + n_cache * fe * es, dtype, (int)B, (int)Cin, (int)Cin, (int)t,
+                                 (int)h, (int)w, st);
+    if (e != hipSuccess) rc = fail(WANVAE_EHIP, "layout conversion: %s", hipGetErrorString(e));
+    for (int k = 0; k < n_cache + t; ++k) in.push((char*)xin + k * fe * es, hw * Cin);
+    out = frames_of(yout, (int)t, B * hw * Cout, hw * Cout, es);
+  } else if (rc == WANVAE_OK) {
+    // [B, frames, h, w, C]: frame k of batch b at base + (b * frames + k) * hwC; read and written in place
+    for (int k = 0; k < n_cache; ++k) in.push((char*)cache + k * hw * Cin * es, n_cache * hw * Cin);
+    for (int k = 0; k < t; ++k) in.push((char*)x + k * hw * Cin * es, t * hw * Cin);
+    out = frames_of(y, (int)t, hw * Cout, t * hw * Cout, es);
+  }
+  if (rc == WANVAE_OK) {
+    ConvCall cc;
+    cc.a.mode = kEpiFrames;
+    set_out(cc.a, out, Cout);
+    rc = run_conv(cw, in, (int)B, (int)h, (int)w, (int)h, (int)w, (int)t, false, cc, dtype, st);
+  }
+  if (rc == WANVAE_OK && layout == WANVAE_NCTHW) {
+    hipError_t e = launch_frames_to_ncthw(yout, y, dtype, (int)B, Cout, (int)t, (int)h, (int)w, st);
+    if (e != hipSuccess) rc = fail(WANVAE_EHIP, "y layout: %s", hipGetErrorString(e));
+  }
+  if (!workspace) {
+    hipError_t e = hipFreeAsync(ws, st);
+    if (rc == WANVAE_OK && e != hipSuccess) rc = fail(WANVAE_EHIP, "hipFreeAsync: %s", hipGetErrorString(e));
+  }
+  return rc;
+}
+
+// ---------------------------------------------------------------- attention block
+
+static int attn_validate(const void* x, int32_t layout, int64_t B, int64_t C, int64_t T, int64_t h, int64_t w,
+                         const wanvae_tensor* gamma, const wanvae_tensor* qkv_w, const wanvae_tensor* qkv_b,
+                         const wanvae_tensor* proj_w, const wanvae_tensor* proj_b, int32_t dtype, const void* y) {
+  if (int rc = check_dtype(dtype, "dtype")) return rc;
+  if (layout != WANVAE_NCTHW && layout != WANVAE_NTHWC) return fail(WANVAE_EARG, "layout %d unknown", layout);
+  if (!x || !y) return fail(WANVAE_EARG, "x and y must not be NULL");
+  if (x == y) return fail(WANVAE_EARG, "y must not alias x");
+  const wanvae_tensor* ts[5] = {gamma, qkv_w, qkv_b, proj_w, proj_b};
+  const char* nm[5] = {"gamma", "qkv_w", "qkv_b", "proj_w", "proj_b"};
+  for (int i = 0; i < 5; ++i)
+    if (int rc = check_tensor(ts[i], nm[i])) return rc;
+  if (B < 1 || T < 1 || h < 1 || w < 1 || C < 1) return fail(WANVAE_ESHAPE, "B, C, T, h, w must be >= 1");
+  if (C % 64 != 0 || C > 1024 || !attn_supported((int)C, dtype))
+    return fail(WANVAE_ESHAPE, "C %lld unsupported (64, 128, 256, 512 or 1024)", (long long)C);
+  if (numel(gamma) != C) return fail(WANVAE_ESHAPE, "gamma has %lld elements, expected %lld", (long long)numel(gamma), (long long)C);
+  if (!(shape_is(qkv_w, {3 * C, C, 1, 1}) || shape_is(qkv_w, {3 * C, C})))
+    return fail(WANVAE_ESHAPE, "qkv_w %s, expected [%lld, %lld, 1, 1]", shape_str(qkv_w).c_str(), (long long)(3 * C), (long long)C);
+  if (!shape_is(qkv_b, {3 * C})) return fail(WANVAE_ESHAPE, "qkv_b %s", shape_str(qkv_b).c_str());
+  if (!(shape_is(proj_w, {C, C, 1, 1}) || shape_is(proj_w, {C, C})))
+    return fail(WANVAE_ESHAPE, "proj_w %s, expected [%lld, %lld, 1, 1]", shape_str(proj_w).c_str(), (long long)C, (long long)C);
+  if (!shape_is(proj_b, {C})) return fail(WANVAE_ESHAPE, "proj_b %s", shape_str(proj_b).c_str());
+  if (B * T * h * w * 3 * C > ((int64_t)1 << 31)) return fail(WANVAE_ESHAPE, "input too large");
+  return WANVAE_OK;
+}
+
+static size_t attn_ws(int64_t B, int64_t C, int64_t T, int64_t h, int64_t w, int32_t layout, int32_t dtype) {
+  Arena ar;
+  const size_t es = esize(dtype);
+  ar.take((size_t)3 * C * C * es);
+  ar.take((size_t)3 * C * 4);
+  ar.take((size_t)C * C * es);
+  ar.take((size_t)C * 4);
+  ar.take((size_t)C * 4);
+  AttnBufs ab;
+  plan_attn_bufs(ar, ab, (int)(B * T), (int)(h * w), (int)C, dtype);
+  if (layout == WANVAE_NCTHW) {
+    ar.take((size_t)B * T * h * w * C * es);
+    ar.take((size_t)B * T * h * w * C * es);
+  }
+  return ar.used;
+}
+
+int wanvae_attn_block_workspace_size(int64_t B, int64_t C, int64_t T, int64_t h, int64_t w, int32_t layout,
+                                     int32_t dtype, size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(WANVAE_EARG, "bytes: NULL");
+  if (int rc = check_dtype(dtype, "dtype")) return rc;
+  *bytes = attn_ws(B, C, T, h, w, layout, dtype);
+  return WANVAE_OK;
+}
+
+int wanvae_attn_block(const void* x, int32_t layout, int64_t B, int64_t C, int64_t T, int64_t h, int64_t w,
+                      const wanvae_tensor* gamma, const wanvae_tensor* qkv_w, const wanvae_tensor* qkv_b,
+                      const wanvae_tensor* proj_w, const wanvae_tensor* proj_b, int32_t dtype, void* y,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (int rc = attn_validate(x, layout, B, C, T, h, w, gamma, qkv_w, qkv_b, proj_w, proj_b, dtype, y)) return rc;
+  const size_t need = attn_ws(B, C, T, h, w, layout, dtype);
+  if (workspace && workspace_bytes < need)
+    return fail(WANVAE_EWORKSPACE, "workspace of %zu bytes, the block needs %zu", workspace_bytes, need);
+  hipStream_t st = (hipStream_t)stream;
+  void* ws = workspace;
+  if (!ws) HIP_TRY(hipMallocAsync(&ws, need, st));
+  Arena ar;
+  ar.base = (char*)ws;
+  const size_t es = esize(dtype);
+  const int Ci = (int)C, nfr = (int)(B * T), S = (int)(h * w);
+  int rc = WANVAE_OK;
+  ConvW qkv, proj;
+  float* g = nullptr;
+  rc = prep_conv(ar, dtype, qkv_w, qkv_b, 3 * Ci, Ci, 1, 1, 1, qkv, st);
+  if (rc == WANVAE_OK) rc = prep_conv(ar, dtype, proj_w, proj_b, Ci, Ci, 1, 1, 1, proj, st);
+  if (rc == WANVAE_OK) rc = prep_vec(ar, dtype, gamma, Ci, g, st);
+  AttnBufs ab;
+  plan_attn_bufs(ar, ab, nfr, S, Ci, dtype);
+  // frames folded into the batch: frame index b' = t * B + b (NCTHW, converted) or b * T + t (NTHWC)
+  const void* xf = x;
+  void* yf = y;
+  if (rc == WANVAE_OK && layout == WANVAE_NCTHW) {
+    void* xb = ar.take((size_t)nfr * S * Ci * es);
+    yf = ar.take((size_t)nfr * S * Ci * es);
+    hipError_t e = launch_ncthw_to_frames(x, dtype, xb, dtype, (int)B, Ci, Ci, (int)T, (int)h, (int)w, st);
+    if (e != hipSuccess) rc = fail(WANVAE_EHIP, "x layout: %s", hipGetErrorString(e));
+    xf = xb;
+  }
+  if (rc == WANVAE_OK) {
+    const FrameRef xr = frames_of(const_cast<void*>(xf), 1, 0, (int64_t)S * Ci, es);
+    const FrameRef yr = frames_of(yf, 1, 0, (int64_t)S * Ci, es);
+    rc = run_attn(xr, yr, nfr, (int)h, (int)w, Ci, g, qkv, proj, ab, dtype, st);
+  }
+  if (rc == WANVAE_OK && layout == WANVAE_NCTHW) {
+    hipError_t e = launch_frames_to_ncthw(yf, y, dtype, (int)B, Ci, (int)T, (int)h, (int)w, st);
+    if (e != hipSuccess) rc = fail(WANVAE_EHIP, "y layout: %s", hipGetErrorString(e));
+  }
+  if (!workspace) {
+    hipError_t e = hipFreeAsync(ws, st);
+    if (rc == WANVAE_OK && e != hipSuccess) rc = fail(WANVAE_EHIP, "hipFreeAsync: %s", hipGetErrorString(e));
+  }
+  return rc;
+}
+
+}  // extern "C"
