@@ -74,7 +74,14 @@ struct AttnArgs {
 };
 
 // Tile shapes of the conv kernel: channels x positions per workgroup.
-enum ConvTile { kTile128x128 = 0, kTile32x256 = 1, kTile256x128 = 2 };
+enum ConvTile {
+  kTile128x128 = 0,  // register-staged loads (bf16 and fp32)
+  kTile32x256 = 1,   // small Cout (conv_out, post_quant_conv)
+  kTile256x128 = 2,
+  kTileDma256x128 = 3,  // bf16, direct-to-LDS pipeline
+  kTileDma256x256 = 4,
+  kTileDma128x128 = 5,
+};
 
 hipError_t launch_conv(const ConvArgs& a, int dtype, int tile, hipStream_t s);
 hipError_t launch_norm(const NormArgs& a, int dtype, hipStream_t s);

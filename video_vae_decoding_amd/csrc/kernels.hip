@@ -153,6 +153,10 @@ __device__ __forceinline__ void conv_epilogue(const ConvArgs& a, int t, int b, i
   }
 }
 
+// 256 bytes of zeros in device memory: the source of every load that stands for padding,
+// a missing history frame or a channel beyond the tensor (never written).
+static __device__ __attribute__((aligned(256))) uint4 g_zero_page[16];
+
 // ------------------------------------------------------------------ implicit-GEMM conv
 //
 // GEMM view: D[n][m] = sum_k W[n][k] * A[m][k], n = output channel, m = output position
@@ -216,35 +220,61 @@ __global__ void __launch_bounds__(256) k_conv(const ConvArgs a) {
     }
   }
 
-  uint4 wr[NWR], ar[NAR];
-  auto gload = [&](int s) {
-    const int tap = s / csteps, cs = s - tap * csteps;
-    const int ci = cs * BK + j * VEC;
-    const int dt = tap / khw, rr = tap - dt * khw, dy = rr / a.kw, dx = rr - dy * a.kw;
-    const bool cok = ci < a.Cin;
-    const T* wb = (const T*)a.w + (int64_t)tap * a.Cin + ci;
+  // K steps in order: taps (dt, dy, dx) major, blocks of BK input channels minor. The cursor
+  // (the next step to load) advances without divisions; per tap it recomputes each A row's
+  // pointer to the tap's input pixel (nullptr where the tap reads zeros).
+  const T* wrow[NWR];
 #pragma unroll
-    for (int i = 0; i < NWR; ++i) {
-      const int n = c0 + r0 + 32 * i;
-      wr[i] = (cok && n < a.Cout) ? *(const uint4*)(wb + n * Ktot) : make_uint4(0, 0, 0, 0);
-    }
+  for (int i = 0; i < NWR; ++i) {
+    const int n = c0 + r0 + 32 * i;
+    wrow[i] = n < a.Cout ? (const T*)a.w + n * Ktot + j * VEC : nullptr;
+  }
+  const T* ap[NAR];
+  int cdt = 0, cdy = 0, cdx = 0, ccs = 0;
+  int64_t woff = 0;
+  auto set_tap = [&]() {
 #pragma unroll
     for (int i = 0; i < NAR; ++i) {
-      const T* base = dt == 0 ? rb0[i] : (dt == 1 ? rb1[i] : rb2[i]);
+      const T* base = cdt == 0 ? rb0[i] : (cdt == 1 ? rb1[i] : rb2[i]);
       int yy, xx;
-      bool ok = cok && base != nullptr;
+      bool ok = base != nullptr;
       if (a.up) {
-        const int yu = ry[i] + dy - ph, xu = rx[i] + dx - pw;
+        const int yu = ry[i] + cdy - ph, xu = rx[i] + cdx - pw;
         ok = ok && yu >= 0 && yu < a.Ho && xu >= 0 && xu < a.Wo;
         yy = yu >> 1;
         xx = xu >> 1;
       } else {
-        yy = ry[i] + dy - ph;
-        xx = rx[i] + dx - pw;
+        yy = ry[i] + cdy - ph;
+        xx = rx[i] + cdx - pw;
         ok = ok && yy >= 0 && yy < a.Hin && xx >= 0 && xx < a.Win;
       }
-      ar[i] = ok ? *(const uint4*)(base + ((int64_t)yy * a.Win + xx) * a.Cin + ci) : make_uint4(0, 0, 0, 0);
+      ap[i] = ok ? base + ((int64_t)yy * a.Win + xx) * a.Cin + j * VEC : nullptr;
     }
+  };
+  auto advance = [&]() {
+    if (++ccs == csteps) {
+      ccs = 0;
+      woff += a.Cin;
+      if (++cdx == a.kw) {
+        cdx = 0;
+        if (++cdy == a.kh) {
+          cdy = 0;
+          ++cdt;
+        }
+      }
+      set_tap();
+    }
+  };
+  uint4 wr[NWR], ar[NAR];
+  // unconditional 16-byte loads: a lane whose chunk is zero reads the zero page instead
+  const uint4* zero = g_zero_page;
+  auto gload = [&]() {
+    const int cb = ccs * BK;
+    const bool cok = cb + j * VEC < a.Cin;
+#pragma unroll
+    for (int i = 0; i < NWR; ++i) wr[i] = *((cok && wrow[i]) ? (const uint4*)(wrow[i] + woff + cb) : zero);
+#pragma unroll
+    for (int i = 0; i < NAR; ++i) ar[i] = *((cok && ap[i]) ? (const uint4*)(ap[i] + cb) : zero);
   };
   auto sstore = [&](int buf) {
     char* sw = smem + buf * STAGE;
@@ -280,15 +310,228 @@ __global__ void __launch_bounds__(256) k_conv(const ConvArgs a) {
     }
   };
 
-  gload(0);
+  set_tap();
+  gload();
   sstore(0);
   __syncthreads();
   for (int s = 0; s < steps; ++s) {
     const int buf = s & 1;
-    if (s + 1 < steps) gload(s + 1);
+    if (s + 1 < steps) {
+      advance();
+      gload();
+    }
     compute(buf);
     if (s + 1 < steps) sstore(buf ^ 1);
     __syncthreads();
+  }
+
+#pragma unroll
+  for (int ip = 0; ip < TPN; ++ip) {
+    const int m = m0 + wp * WP + ip * 16 + (lane & 15);
+    if (m >= M) continue;
+    const int x = m % a.Wo;
+    int q = m / a.Wo;
+    const int y = q % a.Ho;
+    q /= a.Ho;
+    const int b = q % a.B, t = q / a.B;
+#pragma unroll
+    for (int ic = 0; ic < TCN; ++ic) {
+      const int c = c0 + wc * WC + ic * 16 + 4 * (lane >> 4);
+      if (c >= a.Cout) continue;
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = acc[ic][ip][e] + (c + e < a.Cout ? a.bias[c + e] : 0.f);
+      conv_epilogue<T>(a, t, b, y, x, c, v);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ implicit-GEMM conv, LDS-DMA pipeline (bf16)
+//
+// The same GEMM as k_conv, for bf16 operands, with the global -> LDS copies done by the
+// gfx950 direct-to-LDS loads (global_load_lds_dwordx4: each lane moves 16 bytes from its own
+// global address into LDS at base + 16 * lane, with no register round trip). K steps are 32
+// input channels of one tap (64-byte rows of 4 chunks). STAGES LDS buffers form a pipeline:
+// the loads for step s + STAGES - 1 are in flight while the MFMAs of step s run; each wave
+// waits only for its own loads of step s (s_waitcnt vmcnt) before the workgroup barrier.
+// Rows are stored with their 4 chunks permuted, slot = chunk ^ ((row >> 1) & 3), so that the
+// 16-byte LDS reads of an MFMA fragment (16 rows, one chunk) hit distinct banks. Taps that
+// fall in the padding, on a missing history frame, or beyond Cin/Cout load from a zero page.
+
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+// s_waitcnt immediate (gfx9 encoding): vmcnt <= n, lgkmcnt <= 0, expcnt unconstrained
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+
+template <int TC, int TP, int WGC, int WGP, int STAGES>
+__global__ void __launch_bounds__(64 * WGC * WGP) k_conv_dma(const ConvArgs a) {
+  using T = bf16_t;
+  constexpr int NWAVE = WGC * WGP;
+  constexpr int ROWB = 64;                       // 32 bf16 per row per step
+  constexpr int WC = TC / WGC, WP = TP / WGP;    // wave tile
+  constexpr int TCN = WC / 16, TPN = WP / 16;
+  constexpr int NIW = TC / (16 * NWAVE);         // DMA instructions per wave per step (W, A)
+  constexpr int NIA = TP / (16 * NWAVE);
+  constexpr int NI = NIW + NIA;
+  constexpr int SW = TC * ROWB, SA = TP * ROWB, STAGE = SW + SA;
+  static_assert(NIW * 16 * NWAVE == TC && NIA * 16 * NWAVE == TP, "tile / wave mismatch");
+  static_assert(STAGES >= 2 && STAGES <= 4, "stages");
+  __shared__ __attribute__((aligned(1024))) char s0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char s1[STAGE];
+  __shared__ __attribute__((aligned(1024))) char s2[STAGES > 2 ? STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) char s3[STAGES > 3 ? STAGE : 16];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int HWo = a.Ho * a.Wo;
+  const int M = a.F * a.B * HWo;
+  const int nct = (a.Cout + TC - 1) / TC;
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int ct = bid % nct, pt = bid / nct;
+  const int c0 = ct * TC, m0 = pt * TP;
+  const int khw = a.kh * a.kw, taps = a.kt * khw;
+  const int csteps = (a.Cin + 31) / 32;
+  const int steps = taps * csteps;
+  const int64_t Ktot = (int64_t)taps * a.Cin;
+  const int ph = a.kh >> 1, pw = a.kw >> 1;
+  const char* zero = (const char*)g_zero_page;
+
+  // this lane's DMA slots: row r = base + lane / 4, slot lane % 4 holding chunk slot ^ swz
+  const int lrow = lane >> 2, lslot = lane & 3;
+  const int lchunk = lslot ^ ((lrow >> 1) & 3);
+  // W rows: instruction i covers tile rows (wave * NIW + i) * 16 .. + 15
+  const T* wrow[NIW];
+#pragma unroll
+  for (int i = 0; i < NIW; ++i) {
+    const int n = c0 + (wave * NIW + i) * 16 + lrow;
+    wrow[i] = n < a.Cout ? (const T*)a.w + n * Ktot + lchunk * 8 : nullptr;
+  }
+  // A rows: position, and its frame for each time tap
+  const T* rb0[NIA];
+  const T* rb1[NIA];
+  const T* rb2[NIA];
+  int ry[NIA], rx[NIA];
+#pragma unroll
+  for (int i = 0; i < NIA; ++i) {
+    const int m = m0 + (wave * NIA + i) * 16 + lrow;
+    rb0[i] = rb1[i] = rb2[i] = nullptr;
+    ry[i] = rx[i] = 0;
+    if (m < M) {
+      const int x = m % a.Wo;
+      int q = m / a.Wo;
+      const int y = q % a.Ho;
+      q /= a.Ho;
+      const int b = q % a.B, t = q / a.B;
+      ry[i] = y;
+      rx[i] = x;
+      const T* p0 = (const T*)a.in[t];
+      rb0[i] = p0 ? p0 + b * a.in_bs[t] : nullptr;
+      if (a.kt > 1) {
+        const T* p1 = (const T*)a.in[t + 1];
+        const T* p2 = (const T*)a.in[t + 2];
+        rb1[i] = p1 ? p1 + b * a.in_bs[t + 1] : nullptr;
+        rb2[i] = p2 ? p2 + b * a.in_bs[t + 2] : nullptr;
+      }
+    }
+  }
+
+  // issue cursor: the next K step to load (taps major, 32-channel blocks minor), advanced
+  // without divisions; per tap each A row's pointer to its input pixel (nullptr: zeros)
+  const T* ap[NIA];
+  int cdt = 0, cdy = 0, cdx = 0, ccs = 0;
+  int64_t woff = 0;
+  auto set_tap = [&]() {
+#pragma unroll
+    for (int i = 0; i < NIA; ++i) {
+      const T* base = cdt == 0 ? rb0[i] : (cdt == 1 ? rb1[i] : rb2[i]);
+      int yy, xx;
+      bool ok = base != nullptr;
+      if (a.up) {
+        const int yu = ry[i] + cdy - ph, xu = rx[i] + cdx - pw;
+        ok = ok && yu >= 0 && yu < a.Ho && xu >= 0 && xu < a.Wo;
+        yy = yu >> 1;
+        xx = xu >> 1;
+      } else {
+        yy = ry[i] + cdy - ph;
+        xx = rx[i] + cdx - pw;
+        ok = ok && yy >= 0 && yy < a.Hin && xx >= 0 && xx < a.Win;
+      }
+      ap[i] = ok ? base + ((int64_t)yy * a.Win + xx) * a.Cin + lchunk * 8 : nullptr;
+    }
+  };
+  auto advance = [&]() {
+    if (++ccs == csteps) {
+      ccs = 0;
+      woff += a.Cin;
+      if (++cdx == a.kw) {
+        cdx = 0;
+        if (++cdy == a.kh) {
+          cdy = 0;
+          ++cdt;
+        }
+      }
+      set_tap();
+    }
+  };
+  auto issue = [&](char* buf) {
+    const int cb = ccs * 32;
+    const bool cok = cb + lchunk * 8 < a.Cin;
+#pragma unroll
+    for (int i = 0; i < NIW; ++i) {
+      const char* src = (cok && wrow[i]) ? (const char*)(wrow[i] + woff + cb) : zero;
+      __builtin_amdgcn_global_load_lds((const void*)src, LDS_PTR(buf + (wave * NIW + i) * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NIA; ++i) {
+      const char* src = (cok && ap[i]) ? (const char*)(ap[i] + cb) : zero;
+      __builtin_amdgcn_global_load_lds((const void*)src, LDS_PTR(buf + SW + (wave * NIA + i) * 1024), 16, 0, 0);
+    }
+    advance();
+  };
+
+  const int wc = wave / WGP, wp = wave % WGP;
+  f32x4_t acc[TCN][TPN];
+#pragma unroll
+  for (int ic = 0; ic < TCN; ++ic)
+#pragma unroll
+    for (int ip = 0; ip < TPN; ++ip) acc[ic][ip] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // fragment reads: row base + (lane & 15), logical chunk lane >> 4
+  const int rslot = ((lane >> 4) ^ (((lane & 15) >> 1) & 3)) * 16 + (lane & 15) * ROWB;
+  auto compute = [&](const char* buf) {
+    uint4 wf[TCN], af[TPN];
+#pragma unroll
+    for (int ic = 0; ic < TCN; ++ic) wf[ic] = *(const uint4*)(buf + (wc * WC + ic * 16) * ROWB + rslot);
+#pragma unroll
+    for (int ip = 0; ip < TPN; ++ip) af[ip] = *(const uint4*)(buf + SW + (wp * WP + ip * 16) * ROWB + rslot);
+#pragma unroll
+    for (int ic = 0; ic < TCN; ++ic)
+#pragma unroll
+      for (int ip = 0; ip < TPN; ++ip) Mma<T>::run(acc[ic][ip], wf[ic], af[ip]);
+  };
+  char* bufs[4] = {s0, s1, s2, s3};
+
+  set_tap();
+#pragma unroll
+  for (int p = 0; p < STAGES - 1; ++p)
+    if (p < steps) issue(bufs[p]);
+  for (int sb = 0; sb < steps; sb += STAGES) {
+#pragma unroll
+    for (int u = 0; u < STAGES; ++u) {
+      const int s = sb + u;
+      if (s < steps) {
+        // this wave's loads of step s are done once at most the later steps' are pending
+        if (s + STAGES - 2 < steps)
+          wait_vm_lgkm0<NI * (STAGES - 2)>();
+        else
+          wait_vm_lgkm0<0>();
+        __builtin_amdgcn_s_barrier();
+        if (s + STAGES - 1 < steps) issue(bufs[(u + STAGES - 1) % STAGES]);
+        compute(bufs[u]);
+      }
+    }
   }
 
 #pragma unroll
@@ -597,8 +840,19 @@ static hipError_t conv_go(const ConvArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int TC, int TP, int WGC, int WGP, int STAGES>
+static hipError_t conv_dma_go(const ConvArgs& a, hipStream_t s) {
+  const int64_t M = (int64_t)a.F * a.B * a.Ho * a.Wo;
+  const int64_t blocks = ((a.Cout + TC - 1) / TC) * ((M + TP - 1) / TP);
+  hipLaunchKernelGGL((k_conv_dma<TC, TP, WGC, WGP, STAGES>), dim3((unsigned)blocks), dim3(64 * WGC * WGP), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_conv(const ConvArgs& a, int dtype, int tile, hipStream_t s) {
   if (dtype == kBF16) {
+    if (tile == kTileDma256x128) return conv_dma_go<256, 128, 2, 2, 3>(a, s);
+    if (tile == kTileDma256x256) return conv_dma_go<256, 256, 2, 2, 4>(a, s);
+    if (tile == kTileDma128x128) return conv_dma_go<128, 128, 2, 2, 4>(a, s);
     if (tile == kTile32x256) return conv_go<bf16_t, 32, 256>(a, s);
     if (tile == kTile256x128) return conv_go<bf16_t, 256, 128>(a, s);
     return conv_go<bf16_t, 128, 128>(a, s);

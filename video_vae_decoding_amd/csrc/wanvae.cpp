@@ -326,6 +326,19 @@ static int prep_vec(Arena& ar, int dtype, const wanvae_tensor* g, int C, float*&
   return WANVAE_OK;
 }
 
+// Tile of the conv kernel for a layer. WANVAE_CONV_TILE (a ConvTile value) overrides the
+// choice for the bf16 layers with more than 64 output channels, for tuning.
+static int pick_tile(int Cout, int dtype) {
+  static const int forced = [] {
+    const char* e = getenv("WANVAE_CONV_TILE");
+    return e ? atoi(e) : -1;
+  }();
+  if (Cout <= 64) return kTile32x256;
+  if (dtype != kBF16) return kTile128x128;
+  if (forced >= 0) return forced;
+  return kTileDma128x128;
+}
+
 struct ConvCall {
   ConvArgs a;
   ConvCall() { memset(&a, 0, sizeof a); }
@@ -347,7 +360,7 @@ static int run_conv(const ConvW& cw, const FrameRef& in, int B, int Hin, int Win
   a.F = F;
   a.w = cw.w;
   a.bias = cw.b;
-  const int tile = cw.Cout <= 64 ? kTile32x256 : kTile128x128;
+  const int tile = pick_tile(cw.Cout, dtype);
   // algorithmic FLOPs: every output, every spatial tap, the time taps on real frames
   double taps_real = 0;
   for (int t = 0; t < F; ++t)
