@@ -81,6 +81,7 @@ enum ConvTile {
   kTileDma256x128 = 3,  // bf16, direct-to-LDS pipeline
   kTileDma256x256 = 4,
   kTileDma128x128 = 5,
+  kTileDma128x256 = 6,
 };
 
 hipError_t launch_conv(const ConvArgs& a, int dtype, int tile, hipStream_t s);

@@ -346,6 +346,68 @@ __global__ void __launch_bounds__(256) k_conv(const ConvArgs a) {
   }
 }
 
+// 8 consecutive output channels c..c+7 (already bias-added and rounded to bf16) at (t, b, y, x):
+// residual and DupUp3D sums (each rounded) and the store, for the frame / interleave / q-k-vT
+// epilogues. Requires Cout and outC multiples of 8.
+__device__ __forceinline__ uint4 pack8_bf16(const float v[8]) {
+  uint4 r;
+  r.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+  r.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+  r.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
+  r.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
+  return r;
+}
+
+__device__ __forceinline__ void unpack8_bf16(const uint4 r, float v[8]) {
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[2 * e] = bf2f(w[e] & 0xffff);
+    v[2 * e + 1] = bf2f(w[e] >> 16);
+  }
+}
+
+__device__ __forceinline__ void epilogue8_bf16(const ConvArgs& a, int t, int b, int y, int x, int c, float v[8]) {
+  using T = bf16_t;
+  const int64_t pix = (int64_t)y * a.Wo + x;
+  if (a.has_res) {
+    float r[8];
+    unpack8_bf16(*(const uint4*)((const T*)a.res[t] + b * a.res_bs[t] + pix * a.outC + c), r);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = bf2f(f2bf(v[e] + r[e]));
+  }
+  if (a.has_dup) {
+    const int ts = t + a.dup_shift, tin = ts / a.dup_ft, sub_t = ts - tin * a.dup_ft;
+    const T* d = (const T*)a.dup[tin] + b * a.dup_bs[tin] + ((int64_t)(y >> 1) * (a.Wo >> 1) + (x >> 1)) * a.dup_C;
+    const int sub = 4 * sub_t + 2 * (y & 1) + (x & 1);
+    float dv[8];
+    if (a.dup_r == 4 * a.dup_ft) {
+      // each input channel repeated over exactly the (ft, 2, 2) sub-positions: channel c
+      unpack8_bf16(*(const uint4*)(d + c), dv);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dv[e] = bf2f(d[(4 * a.dup_ft * (c + e) + sub) / a.dup_r].u);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = bf2f(f2bf(v[e] + dv[e]));
+  }
+  if (a.mode == kEpiFrames) {
+    *(uint4*)((T*)a.out[t] + b * a.out_bs[t] + pix * a.outC + c) = pack8_bf16(v);
+  } else if (a.mode == kEpiInterleave) {
+    const int half = c >= a.outC ? 1 : 0, fr = 2 * t + half;
+    *(uint4*)((T*)a.out[fr] + b * a.out_bs[fr] + pix * a.outC + (c - half * a.outC)) = pack8_bf16(v);
+  } else if (a.mode == kEpiQKV) {
+    const int C = a.outC, fr = t * a.B + b;
+    if (c < 2 * C) {
+      *(uint4*)((T*)(c < C ? a.q : a.k) + ((int64_t)fr * a.S + pix) * C + (c < C ? c : c - C)) = pack8_bf16(v);
+    } else {
+      T* o = (T*)a.vt + ((int64_t)fr * C + (c - 2 * C)) * a.Sp + pix;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[(int64_t)e * a.Sp].u = f2bf(v[e]);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ implicit-GEMM conv, LDS-DMA pipeline (bf16)
 //
 // The same GEMM as k_conv, for bf16 operands, with the global -> LDS copies done by the
@@ -367,8 +429,8 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
 }
 
-template <int TC, int TP, int WGC, int WGP, int STAGES>
-__global__ void __launch_bounds__(64 * WGC * WGP) k_conv_dma(const ConvArgs a) {
+template <int TC, int TP, int WGC, int WGP, int STAGES, int MINB>
+__global__ void __launch_bounds__(64 * WGC * WGP, MINB) k_conv_dma(const ConvArgs a) {
   using T = bf16_t;
   constexpr int NWAVE = WGC * WGP;
   constexpr int ROWB = 64;                       // 32 bf16 per row per step
@@ -534,24 +596,57 @@ __global__ void __launch_bounds__(64 * WGC * WGP) k_conv_dma(const ConvArgs a) {
     }
   }
 
+  // Epilogue through LDS. Each lane rounds acc + bias to bf16 and writes its 4 channels of
+  // one position into the C tile held in the (now idle) stage buffers: rows are positions of
+  // TC channels, 8-byte slots permuted by slot ^ (row & 15) so the 16 positions of a fragment
+  // hit distinct banks. Then all threads finish 8-channel units (16-byte coalesced reads of
+  // the residual and stores of the result).
+  constexpr int RB = TC * 2;
+  constexpr int RPA = STAGE / RB;
+  static_assert(RPA * STAGES >= TP, "the C tile must fit the stage buffers");
+  auto crow = [&](int r) -> char* {
+    char* base = r < RPA ? s0 : (r < 2 * RPA ? s1 : (r < 3 * RPA ? s2 : s3));
+    return base + (r % RPA) * RB;
+  };
+  __syncthreads();
 #pragma unroll
   for (int ip = 0; ip < TPN; ++ip) {
-    const int m = m0 + wp * WP + ip * 16 + (lane & 15);
-    if (m >= M) continue;
+    const int p = wp * WP + ip * 16 + (lane & 15);
+    char* row = crow(p);
+#pragma unroll
+    for (int ic = 0; ic < TCN; ++ic) {
+      const int c = wc * WC + ic * 16 + 4 * (lane >> 4);
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = acc[ic][ip][e] + (c0 + c + e < a.Cout ? a.bias[c0 + c + e] : 0.f);
+      uint2 pk;
+      pk.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+      pk.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+      *(uint2*)(row + (((c >> 2) ^ (p & 15)) << 3)) = pk;
+    }
+  }
+  __syncthreads();
+  constexpr int UPR = TC / 8;
+  for (int u = tid; u < TP * UPR; u += 64 * NWAVE) {
+    const int p = u / UPR, cu = u % UPR;
+    const int m = m0 + p, c = c0 + cu * 8;
+    if (m >= M || c >= a.Cout) continue;
+    const char* row = crow(p);
+    const uint2 lo = *(const uint2*)(row + (((2 * cu) ^ (p & 15)) << 3));
+    const uint2 hi = *(const uint2*)(row + (((2 * cu + 1) ^ (p & 15)) << 3));
+    const uint32_t w4[4] = {lo.x, lo.y, hi.x, hi.y};
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = bf2f(w4[e] & 0xffff);
+      v[2 * e + 1] = bf2f(w4[e] >> 16);
+    }
     const int x = m % a.Wo;
     int q = m / a.Wo;
     const int y = q % a.Ho;
     q /= a.Ho;
     const int b = q % a.B, t = q / a.B;
-#pragma unroll
-    for (int ic = 0; ic < TCN; ++ic) {
-      const int c = c0 + wc * WC + ic * 16 + 4 * (lane >> 4);
-      if (c >= a.Cout) continue;
-      float v[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = acc[ic][ip][e] + (c + e < a.Cout ? a.bias[c + e] : 0.f);
-      conv_epilogue<T>(a, t, b, y, x, c, v);
-    }
+    epilogue8_bf16(a, t, b, y, x, c, v);
   }
 }
 
@@ -840,19 +935,20 @@ static hipError_t conv_go(const ConvArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int TC, int TP, int WGC, int WGP, int STAGES>
+template <int TC, int TP, int WGC, int WGP, int STAGES, int MINB>
 static hipError_t conv_dma_go(const ConvArgs& a, hipStream_t s) {
   const int64_t M = (int64_t)a.F * a.B * a.Ho * a.Wo;
   const int64_t blocks = ((a.Cout + TC - 1) / TC) * ((M + TP - 1) / TP);
-  hipLaunchKernelGGL((k_conv_dma<TC, TP, WGC, WGP, STAGES>), dim3((unsigned)blocks), dim3(64 * WGC * WGP), 0, s, a);
+  hipLaunchKernelGGL((k_conv_dma<TC, TP, WGC, WGP, STAGES, MINB>), dim3((unsigned)blocks), dim3(64 * WGC * WGP), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_conv(const ConvArgs& a, int dtype, int tile, hipStream_t s) {
   if (dtype == kBF16) {
-    if (tile == kTileDma256x128) return conv_dma_go<256, 128, 2, 2, 3>(a, s);
-    if (tile == kTileDma256x256) return conv_dma_go<256, 256, 2, 2, 4>(a, s);
-    if (tile == kTileDma128x128) return conv_dma_go<128, 128, 2, 2, 4>(a, s);
+    if (tile == kTileDma256x128) return conv_dma_go<256, 128, 2, 2, 3, 2>(a, s);
+    if (tile == kTileDma256x256) return conv_dma_go<256, 256, 2, 2, 4, 1>(a, s);
+    if (tile == kTileDma128x256) return conv_dma_go<128, 256, 2, 2, 3, 2>(a, s);
+    if (tile == kTileDma128x128) return conv_dma_go<128, 128, 2, 2, 4, 2>(a, s);
     if (tile == kTile32x256) return conv_go<bf16_t, 32, 256>(a, s);
     if (tile == kTile256x128) return conv_go<bf16_t, 256, 128>(a, s);
     return conv_go<bf16_t, 128, 128>(a, s);

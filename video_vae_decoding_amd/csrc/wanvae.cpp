@@ -328,15 +328,18 @@ static int prep_vec(Arena& ar, int dtype, const wanvae_tensor* g, int C, float*&
 
 // Tile of the conv kernel for a layer. WANVAE_CONV_TILE (a ConvTile value) overrides the
 // choice for the bf16 layers with more than 64 output channels, for tuning.
-static int pick_tile(int Cout, int dtype) {
+static int pick_tile(int Cout, int64_t M, int mode, int dtype) {
   static const int forced = [] {
     const char* e = getenv("WANVAE_CONV_TILE");
     return e ? atoi(e) : -1;
   }();
-  if (Cout <= 64) return kTile32x256;
-  if (dtype != kBF16) return kTile128x128;
+  // the direct-to-LDS bf16 kernels take every epilogue but the video one, Cout % 8 == 0
+  const bool dma_ok = dtype == kBF16 && mode != kEpiVideo && Cout % 8 == 0 && Cout > 64;
+  if (!dma_ok) return Cout <= 64 ? kTile32x256 : kTile128x128;
   if (forced >= 0) return forced;
-  return kTileDma128x128;
+  // 256 x 128 tiles (128 x 64 per wave) where there are enough positions to fill the chip;
+  // 128 x 128 on the level-0 layers (3,520 positions per frame)
+  return M >= 16384 ? kTileDma256x128 : kTileDma128x128;
 }
 
 struct ConvCall {
@@ -360,7 +363,7 @@ static int run_conv(const ConvW& cw, const FrameRef& in, int B, int Hin, int Win
   a.F = F;
   a.w = cw.w;
   a.bias = cw.b;
-  const int tile = pick_tile(cw.Cout, dtype);
+  const int tile = pick_tile(cw.Cout, (int64_t)F * B * Ho * Wo, a.mode, dtype);
   // algorithmic FLOPs: every output, every spatial tap, the time taps on real frames
   double taps_real = 0;
   for (int t = 0; t < F; ++t)
