@@ -82,6 +82,7 @@ enum ConvTile {
   kTileDma256x256 = 4,
   kTileDma128x128 = 5,
   kTileDma128x256 = 6,
+  kTileDma16x256 = 7,   // bf16, small Cout (conv_out)
 };
 
 hipError_t launch_conv(const ConvArgs& a, int dtype, int tile, hipStream_t s);

@@ -29,12 +29,15 @@ struct bf16_t {
 
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// float -> bfloat16, round to nearest even; NaN stays NaN
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
+
+// float -> bfloat16, round to nearest even, NaN stays NaN (gfx950's v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+// two floats -> two bfloat16 in one 32-bit word (low half = a), one conversion instruction
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
 template <typename T>
@@ -61,8 +64,8 @@ struct Elem<bf16_t> {
   }
   static __device__ __forceinline__ void st4(bf16_t* p, const float v[4]) {
     uint2 x;
-    x.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-    x.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+    x.x = pack2_bf16(v[0], v[1]);
+    x.y = pack2_bf16(v[2], v[3]);
     *(uint2*)p = x;
   }
 };
@@ -351,10 +354,10 @@ __global__ void __launch_bounds__(256) k_conv(const ConvArgs a) {
 // epilogues. Requires Cout and outC multiples of 8.
 __device__ __forceinline__ uint4 pack8_bf16(const float v[8]) {
   uint4 r;
-  r.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-  r.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
-  r.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
-  r.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
+  r.x = pack2_bf16(v[0], v[1]);
+  r.y = pack2_bf16(v[2], v[3]);
+  r.z = pack2_bf16(v[4], v[5]);
+  r.w = pack2_bf16(v[6], v[7]);
   return r;
 }
 
@@ -436,11 +439,16 @@ __global__ void __launch_bounds__(64 * WGC * WGP, MINB) k_conv_dma(const ConvArg
   constexpr int ROWB = 64;                       // 32 bf16 per row per step
   constexpr int WC = TC / WGC, WP = TP / WGP;    // wave tile
   constexpr int TCN = WC / 16, TPN = WP / 16;
-  constexpr int NIW = TC / (16 * NWAVE);         // DMA instructions per wave per step (W, A)
+  // DMA instructions per wave per step (each moves 16 rows): W, A. When the W tile has fewer
+  // than 16 * NWAVE rows, the waves past it load the zero page into a spare LDS slot, so that
+  // every wave has the same number of loads in flight (the vmcnt waits count them).
+  constexpr int NIW = TC >= 16 * NWAVE ? TC / (16 * NWAVE) : 1;
   constexpr int NIA = TP / (16 * NWAVE);
   constexpr int NI = NIW + NIA;
-  constexpr int SW = TC * ROWB, SA = TP * ROWB, STAGE = SW + SA;
-  static_assert(NIW * 16 * NWAVE == TC && NIA * 16 * NWAVE == TP, "tile / wave mismatch");
+  constexpr int SPARE = TC >= 16 * NWAVE ? 0 : 1024;
+  constexpr int SW = TC * ROWB, SA = TP * ROWB, STAGE = SW + SA + SPARE;
+  static_assert((TC < 16 * NWAVE || NIW * 16 * NWAVE == TC) && NIA * 16 * NWAVE == TP, "tile / wave mismatch");
+  static_assert(TC % 16 == 0, "W tile rows");
   static_assert(STAGES >= 2 && STAGES <= 4, "stages");
   __shared__ __attribute__((aligned(1024))) char s0[STAGE];
   __shared__ __attribute__((aligned(1024))) char s1[STAGE];
@@ -466,10 +474,13 @@ __global__ void __launch_bounds__(64 * WGC * WGP, MINB) k_conv_dma(const ConvArg
   const int lchunk = lslot ^ ((lrow >> 1) & 3);
   // W rows: instruction i covers tile rows (wave * NIW + i) * 16 .. + 15
   const T* wrow[NIW];
+  int wdst[NIW];  // LDS offset of the instruction's 16 rows (the spare slot past the W tile)
 #pragma unroll
   for (int i = 0; i < NIW; ++i) {
-    const int n = c0 + (wave * NIW + i) * 16 + lrow;
-    wrow[i] = n < a.Cout ? (const T*)a.w + n * Ktot + lchunk * 8 : nullptr;
+    const int r = (wave * NIW + i) * 16;
+    const int n = c0 + r + lrow;
+    wrow[i] = (r < TC && n < a.Cout) ? (const T*)a.w + n * Ktot + lchunk * 8 : nullptr;
+    wdst[i] = r < TC ? r * ROWB : SW + SA;
   }
   // A rows: position, and its frame for each time tap
   const T* rb0[NIA];
@@ -544,7 +555,7 @@ __global__ void __launch_bounds__(64 * WGC * WGP, MINB) k_conv_dma(const ConvArg
 #pragma unroll
     for (int i = 0; i < NIW; ++i) {
       const char* src = (cok && wrow[i]) ? (const char*)(wrow[i] + woff + cb) : zero;
-      __builtin_amdgcn_global_load_lds((const void*)src, LDS_PTR(buf + (wave * NIW + i) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)src, LDS_PTR(buf + wdst[i]), 16, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < NIA; ++i) {
@@ -603,6 +614,7 @@ __global__ void __launch_bounds__(64 * WGC * WGP, MINB) k_conv_dma(const ConvArg
   // the residual and stores of the result).
   constexpr int RB = TC * 2;
   constexpr int RPA = STAGE / RB;
+  constexpr int SWZ = TC / 4 - 1 < 15 ? TC / 4 - 1 : 15;  // slot permutation mask
   static_assert(RPA * STAGES >= TP, "the C tile must fit the stage buffers");
   auto crow = [&](int r) -> char* {
     char* base = r < RPA ? s0 : (r < 2 * RPA ? s1 : (r < 3 * RPA ? s2 : s3));
@@ -620,33 +632,63 @@ __global__ void __launch_bounds__(64 * WGC * WGP, MINB) k_conv_dma(const ConvArg
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = acc[ic][ip][e] + (c0 + c + e < a.Cout ? a.bias[c0 + c + e] : 0.f);
       uint2 pk;
-      pk.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-      pk.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
-      *(uint2*)(row + (((c >> 2) ^ (p & 15)) << 3)) = pk;
+      pk.x = pack2_bf16(v[0], v[1]);
+      pk.y = pack2_bf16(v[2], v[3]);
+      *(uint2*)(row + (((c >> 2) ^ (p & SWZ)) << 3)) = pk;
     }
   }
   __syncthreads();
-  constexpr int UPR = TC / 8;
-  for (int u = tid; u < TP * UPR; u += 64 * NWAVE) {
-    const int p = u / UPR, cu = u % UPR;
-    const int m = m0 + p, c = c0 + cu * 8;
-    if (m >= M || c >= a.Cout) continue;
-    const char* row = crow(p);
-    const uint2 lo = *(const uint2*)(row + (((2 * cu) ^ (p & 15)) << 3));
-    const uint2 hi = *(const uint2*)(row + (((2 * cu + 1) ^ (p & 15)) << 3));
-    const uint32_t w4[4] = {lo.x, lo.y, hi.x, hi.y};
-    float v[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[2 * e] = bf2f(w4[e] & 0xffff);
-      v[2 * e + 1] = bf2f(w4[e] >> 16);
+  if (a.mode == kEpiVideo) {
+    // unpatchify + clamp, 4 channels per unit (Cout is not a multiple of 8 here)
+    constexpr int UPR4 = TC / 4;
+    for (int u = tid; u < TP * UPR4; u += 64 * NWAVE) {
+      const int p = u / UPR4, cu = u % UPR4;
+      const int m = m0 + p, c = c0 + cu * 4;
+      if (m >= M || c >= a.Cout) continue;
+      const uint2 w2 = *(const uint2*)(crow(p) + ((cu ^ (p & SWZ)) << 3));
+      float v[4] = {bf2f(w2.x & 0xffff), bf2f(w2.x >> 16), bf2f(w2.y & 0xffff), bf2f(w2.y >> 16)};
+      const int x = m % a.Wo;
+      int q = m / a.Wo;
+      const int y = q % a.Ho;
+      q /= a.Ho;
+      const int b = q % a.B, t = q / a.B;
+      conv_epilogue<T>(a, t, b, y, x, c, v);
     }
-    const int x = m % a.Wo;
-    int q = m / a.Wo;
-    const int y = q % a.Ho;
-    q /= a.Ho;
-    const int b = q % a.B, t = q / a.B;
-    epilogue8_bf16(a, t, b, y, x, c, v);
+    return;
+  }
+  // units: 8 channels of one position; a thread's units step through the positions by
+  // PSTEP, so (t, b, y, x) is decoded once and then advanced
+  constexpr int UPR = TC / 8;
+  constexpr int NT = 64 * NWAVE;
+  static_assert(NT % UPR == 0, "units per row must divide the workgroup");
+  constexpr int PSTEP = NT / UPR;
+  const int cu = tid % UPR, c = c0 + cu * 8;
+  int p = tid / UPR;
+  int m = m0 + p;
+  int x = m % a.Wo, q = m / a.Wo;
+  int y = q % a.Ho;
+  q /= a.Ho;
+  int b = q % a.B, t = q / a.B;
+  for (; p < TP && m < M; p += PSTEP, m += PSTEP) {
+    if (c < a.Cout) {
+      const char* row = crow(p);
+      const uint2 lo = *(const uint2*)(row + (((2 * cu) ^ (p & SWZ)) << 3));
+      const uint2 hi = *(const uint2*)(row + (((2 * cu + 1) ^ (p & SWZ)) << 3));
+      float v[8];
+      unpack8_bf16(make_uint4(lo.x, lo.y, hi.x, hi.y), v);
+      epilogue8_bf16(a, t, b, y, x, c, v);
+    }
+    x += PSTEP;
+    while (x >= a.Wo) {
+      x -= a.Wo;
+      if (++y == a.Ho) {
+        y = 0;
+        if (++b == a.B) {
+          b = 0;
+          ++t;
+        }
+      }
+    }
   }
 }
 
@@ -695,6 +737,96 @@ __global__ void __launch_bounds__(256) k_norm(const NormArgs a) {
         o[e] = u;
       }
       X::st4(y + c, o);
+    }
+  }
+}
+
+// Bandwidth-oriented version: a position's C channels are spread over LPP lanes, each lane
+// holding VPL 16-byte vectors; a wave covers 64 / LPP positions per round and R rounds, all
+// loads issued before the sums are reduced (xor shuffles within the LPP lanes).
+template <typename T, int LPP, int VPL, int R>
+__global__ void __launch_bounds__(256) k_norm_v(const NormArgs a) {
+  using X = Elem<T>;
+  constexpr int EV = 16 / (int)sizeof(T);  // elements per 16-byte vector
+  constexpr int PPW = 64 / LPP;
+  // grid: x = position blocks within a frame, y = (frame t, batch b)
+  const int lane = threadIdx.x & 63, li = lane % LPP;
+  const int t = blockIdx.y / a.B, b = blockIdx.y % a.B;
+  const int pos0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * PPW * R + lane / LPP;
+  const T* xf = (const T*)a.in[t] + b * a.in_bs[t];
+  T* yf = (T*)a.out[t] + b * a.out_bs[t];
+  // this lane's gamma values (its channels are the same in every round)
+  float g[VPL][EV];
+#pragma unroll
+  for (int v = 0; v < VPL; ++v)
+#pragma unroll
+    for (int e = 0; e < EV; e += 4) {
+      const float4 q = *(const float4*)(a.gamma + (v * LPP + li) * EV + e);
+      g[v][e] = q.x, g[v][e + 1] = q.y, g[v][e + 2] = q.z, g[v][e + 3] = q.w;
+    }
+  uint4 buf[R][VPL];
+  T* outp[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int pos = pos0 + r * PPW;
+    outp[r] = nullptr;
+    if (pos < a.HW) {
+      const T* x = xf + (int64_t)pos * a.C;
+      outp[r] = yf + (int64_t)pos * a.C;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) buf[r][v] = *(const uint4*)(x + (v * LPP + li) * EV);
+    } else {
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) buf[r][v] = make_uint4(0, 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float val[VPL][EV];
+    float ss = 0.f;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      if constexpr (sizeof(T) == 2) {
+        unpack8_bf16(buf[r][v], val[v]);
+      } else {
+        val[v][0] = __uint_as_float(buf[r][v].x), val[v][1] = __uint_as_float(buf[r][v].y);
+        val[v][2] = __uint_as_float(buf[r][v].z), val[v][3] = __uint_as_float(buf[r][v].w);
+      }
+#pragma unroll
+      for (int e = 0; e < EV; ++e) ss += val[v][e] * val[v][e];
+    }
+#pragma unroll
+    for (int off = LPP / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+    if (!outp[r]) continue;
+    const float d = fmaxf(sqrtf(ss), 1e-12f);
+    const float inv = 1.f / d;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const int c0 = (v * LPP + li) * EV;
+      float o[EV];
+#pragma unroll
+      for (int e = 0; e < EV; ++e) {
+        float u;
+        if constexpr (sizeof(T) == 2) {
+          // bf16: reciprocal multiply, hardware exp2 and reciprocal; each differs from the
+          // correctly rounded fp32 operation by a few fp32 ulp, below the bf16 rounding
+          u = X::R(val[v][e] * inv);
+          u = X::R(u * a.sqrtC);
+          u = X::R(u * g[v][e]);
+          if (a.silu) u = X::R(u * __builtin_amdgcn_rcpf(1.f + __expf(-u)));
+        } else {
+          u = val[v][e] / d;
+          u = u * a.sqrtC;
+          u = u * g[v][e];
+          if (a.silu) u = u / (1.f + expf(-u));
+        }
+        o[e] = u;
+      }
+      if constexpr (sizeof(T) == 2) {
+        *(uint4*)(outp[r] + c0) = pack8_bf16(o);
+      } else {
+        *(float4*)(outp[r] + c0) = make_float4(o[0], o[1], o[2], o[3]);
+      }
     }
   }
 }
@@ -808,10 +940,10 @@ __global__ void __launch_bounds__(64 * NW) k_attn(const AttnArgs a) {
       uint4 pb[2];
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
-        pb[qt].x = (uint32_t)f2bf(p[0][qt][0]) | ((uint32_t)f2bf(p[0][qt][1]) << 16);
-        pb[qt].y = (uint32_t)f2bf(p[0][qt][2]) | ((uint32_t)f2bf(p[0][qt][3]) << 16);
-        pb[qt].z = (uint32_t)f2bf(p[1][qt][0]) | ((uint32_t)f2bf(p[1][qt][1]) << 16);
-        pb[qt].w = (uint32_t)f2bf(p[1][qt][2]) | ((uint32_t)f2bf(p[1][qt][3]) << 16);
+        pb[qt].x = pack2_bf16(p[0][qt][0], p[0][qt][1]);
+        pb[qt].y = pack2_bf16(p[0][qt][2], p[0][qt][3]);
+        pb[qt].z = pack2_bf16(p[1][qt][0], p[1][qt][1]);
+        pb[qt].w = pack2_bf16(p[1][qt][2], p[1][qt][3]);
       }
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
@@ -949,6 +1081,7 @@ hipError_t launch_conv(const ConvArgs& a, int dtype, int tile, hipStream_t s) {
     if (tile == kTileDma256x256) return conv_dma_go<256, 256, 2, 2, 4, 1>(a, s);
     if (tile == kTileDma128x256) return conv_dma_go<128, 256, 2, 2, 3, 2>(a, s);
     if (tile == kTileDma128x128) return conv_dma_go<128, 128, 2, 2, 4, 2>(a, s);
+    if (tile == kTileDma16x256) return conv_dma_go<16, 256, 1, 4, 4, 2>(a, s);
     if (tile == kTile32x256) return conv_go<bf16_t, 32, 256>(a, s);
     if (tile == kTile256x128) return conv_go<bf16_t, 256, 128>(a, s);
     return conv_go<bf16_t, 128, 128>(a, s);
@@ -957,7 +1090,37 @@ hipError_t launch_conv(const ConvArgs& a, int dtype, int tile, hipStream_t s) {
   return conv_go<float, 128, 128>(a, s);
 }
 
+template <typename T, int LPP, int VPL>
+static hipError_t norm_v_go(const NormArgs& a, hipStream_t s) {
+  constexpr int R = 4;
+  const int per_block = 4 * (64 / LPP) * R;
+  hipLaunchKernelGGL((k_norm_v<T, LPP, VPL, R>), dim3((unsigned)((a.HW + per_block - 1) / per_block), (unsigned)(a.F * a.B)),
+                     dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_norm(const NormArgs& a, int dtype, hipStream_t s) {
+  if (dtype == kBF16) {
+    switch (a.C) {
+      case 16: return norm_v_go<bf16_t, 2, 1>(a, s);
+      case 32: return norm_v_go<bf16_t, 4, 1>(a, s);
+      case 64: return norm_v_go<bf16_t, 8, 1>(a, s);
+      case 128: return norm_v_go<bf16_t, 16, 1>(a, s);
+      case 256: return norm_v_go<bf16_t, 32, 1>(a, s);
+      case 512: return norm_v_go<bf16_t, 64, 1>(a, s);
+      case 1024: return norm_v_go<bf16_t, 64, 2>(a, s);
+    }
+  } else {
+    switch (a.C) {
+      case 16: return norm_v_go<float, 4, 1>(a, s);
+      case 32: return norm_v_go<float, 8, 1>(a, s);
+      case 64: return norm_v_go<float, 16, 1>(a, s);
+      case 128: return norm_v_go<float, 32, 1>(a, s);
+      case 256: return norm_v_go<float, 64, 1>(a, s);
+      case 512: return norm_v_go<float, 64, 2>(a, s);
+      case 1024: return norm_v_go<float, 64, 4>(a, s);
+    }
+  }
   const int64_t M = (int64_t)a.F * a.B * a.HW;
   const unsigned blocks = (unsigned)((M + 3) / 4);
   if (dtype == kBF16)

@@ -333,7 +333,9 @@ static int pick_tile(int Cout, int64_t M, int mode, int dtype) {
     const char* e = getenv("WANVAE_CONV_TILE");
     return e ? atoi(e) : -1;
   }();
-  // the direct-to-LDS bf16 kernels take every epilogue but the video one, Cout % 8 == 0
+  // bf16: the direct-to-LDS kernels (Cout % 8 == 0 for the frame / interleave / q-k-v stores;
+  // the unpatchify + clamp store of conv_out on the 16-channel tile)
+  if (dtype == kBF16 && mode == kEpiVideo && Cout <= 16 && Cout % 4 == 0) return kTileDma16x256;
   const bool dma_ok = dtype == kBF16 && mode != kEpiVideo && Cout % 8 == 0 && Cout > 64;
   if (!dma_ok) return Cout <= 64 ? kTile32x256 : kTile128x128;
   if (forced >= 0) return forced;
