@@ -9,6 +9,7 @@ from __future__ import annotations
 import math
 
 import numpy as np
+import torch
 
 MODES = ("fp64", "fp32", "bf16")
 CACHE_T = 2           # frames of history a causal conv with a 3-frame kernel keeps ("Causal caches")
@@ -18,16 +19,10 @@ PREFIXES = ("decoder.", "post_quant_conv.")
 
 
 def round_bf16(x) -> np.ndarray:
-    """Round to bfloat16, nearest even, via float32 (as a float32 -> bfloat16 cast does).
-    Returns float32 values that are exactly representable in bfloat16. NaN stays NaN."""
+    """Round to bfloat16, nearest even, via float32 (torch's float32 -> bfloat16 cast, a library
+    primitive). Returns float32 values that are exactly representable in bfloat16; NaN stays NaN."""
     f = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
-    u = f.view(np.uint32).astype(np.uint64)
-    r = (((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16).astype(np.uint32)
-    out = r.view(np.float32).reshape(f.shape)
-    nan = np.isnan(f)
-    if nan.any():
-        out = np.where(nan, np.float32(np.nan), out)
-    return out
+    return torch.from_numpy(f).to(torch.bfloat16).to(torch.float32).numpy()
 
 
 class Prec:
@@ -57,6 +52,19 @@ class Prec:
 
 # ---------------------------------------------------------------- convolution
 
+_POOL: dict = {}
+
+
+def _scratch(role: str, shape, dtype) -> torch.Tensor:
+    """A reused temporary of the conv (allocating multi-GB buffers afresh for every conv costs
+    more than the arithmetic). Contents are undefined."""
+    n = int(np.prod(shape))
+    t = _POOL.get((role, dtype))
+    if t is None or t.numel() < n:
+        _POOL[(role, dtype)] = t = torch.empty(n, dtype=dtype)
+    return t[:n].view(*shape)
+
+
 def causal_conv(x, w, b, hist, P: Prec) -> np.ndarray:
     """WanCausalConv3d ("The parts": causal conv): stride 1, spatial zero padding kh//2, kw//2
     on both sides; in time 2*(kt//2) frames before x, the history ``hist`` first (its last
@@ -78,16 +86,26 @@ def causal_conv(x, w, b, hist, P: Prec) -> np.ndarray:
     xt = np.concatenate(frames, axis=2)
     ph, pw = kh // 2, kw // 2
     xp = np.pad(xt, ((0, 0), (0, 0), (0, 0), (ph, ph), (pw, pw)))
-    xl = np.moveaxis(xp, 1, -1)                      # [B, Tp, Hp, Wp, Ci], channels last
-    acc = np.zeros((B * T * H * W, Co), P.acc_t)
+    Tp, Hp, Wp = xp.shape[2:]
+    tdt = torch.float64 if P.acc_t == np.float64 else torch.float32
+    # channels last, in the accumulation type: [B, Tp, Hp, Wp, Ci] as rows of Ci values
+    xl = _scratch("x", (B, Tp, Hp, Wp, Ci), tdt)
+    xl.copy_(torch.from_numpy(np.ascontiguousarray(xp)).permute(0, 2, 3, 4, 1))
+    xl = xl.view(-1, Ci)
+    z = _scratch("z", (xl.shape[0], Co), tdt)
+    zv = z.view(B, Tp, Hp, Wp, Co)
+    acc = _scratch("acc", (B, T, H, W, Co), tdt).zero_()
+    # the sum over taps: every padded input row times the tap's [Ci, Co] matrix, added to the
+    # output at the tap's shift (output (t, y, x) takes padded row (t + dt, y + dy, x + dx))
     for dt in range(kt):
         for dy in range(kh):
             for dx in range(kw):
-                a = np.ascontiguousarray(xl[:, dt:dt + T, dy:dy + H, dx:dx + W, :], dtype=P.acc_t)
-                acc += a.reshape(-1, Ci) @ np.ascontiguousarray(w[:, :, dt, dy, dx].T, dtype=P.acc_t)
-    acc += np.asarray(b, dtype=P.acc_t)
-    out = np.moveaxis(acc.reshape(B, T, H, W, Co), -1, 1)
-    return np.ascontiguousarray(P.R(out))
+                wt = torch.from_numpy(np.ascontiguousarray(w[:, :, dt, dy, dx].T, dtype=P.acc_t))
+                torch.mm(xl, wt, out=z)
+                acc += zv[:, dt:dt + T, dy:dy + H, dx:dx + W]
+    acc += torch.from_numpy(np.asarray(b, dtype=P.acc_t))
+    out = torch.from_numpy(P.R(acc.numpy()))                  # rounded while contiguous
+    return out.permute(0, 4, 1, 2, 3).contiguous().numpy()
 
 
 def conv_points(xt, w, b, pts, acc_t=np.float64) -> np.ndarray:
@@ -258,21 +276,25 @@ def up_block(x, Wt, i, cache, first, P: Prec) -> np.ndarray:
     return P.R(x.astype(np.float64) + d.astype(np.float64))
 
 
-def decode_chunk(x, Wt, cache, first, P: Prec) -> np.ndarray:
-    """The decoder on one latent frame [B, 48, 1, h, w] -> [B, 12, 1 or 4, 8h, 8w]."""
+def decode_chunk(x, Wt, cache, first, P: Prec, on_step=None) -> np.ndarray:
+    """The decoder on one latent frame [B, 48, 1, h, w] -> [B, 12, 1 or 4, 8h, 8w].
+    on_step(name), if given, is called after each block (progress reporting only)."""
+    step = on_step or (lambda name: None)
     x = cached_conv(x, Wt["decoder.conv_in.weight"], Wt["decoder.conv_in.bias"], "decoder.conv_in", cache, P)
     x = residual_block(x, Wt, "decoder.mid_block.resnets.0", cache, P)
     a = "decoder.mid_block.attentions.0"
     x = attention(x, Wt[f"{a}.norm.gamma"], Wt[f"{a}.to_qkv.weight"], Wt[f"{a}.to_qkv.bias"],
                   Wt[f"{a}.proj.weight"], Wt[f"{a}.proj.bias"], P)
     x = residual_block(x, Wt, "decoder.mid_block.resnets.1", cache, P)
+    step("mid_block")
     for i in range(4):
         x = up_block(x, Wt, i, cache, first, P)
+        step(f"up_block {i}")
     x = silu(rms_norm(x, Wt["decoder.norm_out.gamma"], P), P)
     return cached_conv(x, Wt["decoder.conv_out.weight"], Wt["decoder.conv_out.bias"], "decoder.conv_out", cache, P)
 
 
-def decode(z, weights, mode: str = "fp32", acc: str = "f64", on_chunk=None) -> np.ndarray:
+def decode(z, weights, mode: str = "fp32", acc: str = "f64", on_chunk=None, on_step=None) -> np.ndarray:
     """decode(z [B, 48, T, h, w], weights) -> video [B, 3, 4T-3, 16h, 16w] in [-1, 1].
     Only names under the decoder's prefixes are used; they and z are rounded to the mode's
     type; post_quant_conv runs over all T frames, then the chunk loop, concatenation along
@@ -283,7 +305,8 @@ def decode(z, weights, mode: str = "fp32", acc: str = "f64", on_chunk=None) -> n
     cache: dict = {}
     chunks = []
     for i in range(x.shape[2]):
-        chunks.append(decode_chunk(x[:, :, i:i + 1], Wt, cache, i == 0, P))
+        chunks.append(decode_chunk(x[:, :, i:i + 1], Wt, cache, i == 0, P,
+                                   None if on_step is None else (lambda name, i=i: on_step(i, name))))
         if on_chunk is not None:
             on_chunk(i)
     return clamp(unpatchify(np.concatenate(chunks, axis=2)))

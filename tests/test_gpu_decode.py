@@ -2,9 +2,10 @@
 
 Gates: fp32 max |gpu - oracle| <= 5e-4 on the [-1, 1] video; bf16 max <= 3e-2 and PSNR
 >= 40 dB against the oracle's bf16 mode (the bf16 rounding points of the page's "Precision"
-section). On the tiny decoder (16 to 64 channels) a bf16 decode is more sensitive than that
-to the order of its float32 sums: there the max and mean bound is 1.5x the oracle's own
-difference between float64 and float32 accumulation. The tiny decoder is compared in full; the full-size 704x1280 and 1280x704 decodes
+section). A bf16 decode is more sensitive than that to the order of its float32 sums, on the
+tiny decoder and at full size alike: the oracle's own bf16 decode with float64 and with float32
+sums differs by max 0.029-0.043 (mean 0.004, PSNR 50 dB). So the bf16 max and mean bound is
+1.5x that self-difference (stored for the full-size workloads), with PSNR >= 40 dB. The tiny decoder is compared in full; the full-size 704x1280 and 1280x704 decodes
 on stored oracle samples of their first 5 frames (tests/golden, made by make_golden.py from
 the oracle) and by properties that hold at any size: causality (the first 4k - 3 frames are
 the decode of the first k latent frames) and determinism, bit for bit.
@@ -144,22 +145,37 @@ FULL = [("ti2v5b_landscape", "bf16"), ("ti2v5b_landscape", "fp32"), ("ti2v5b_por
 
 @pytest.mark.parametrize("config,mode", FULL)
 def test_full_decode_first_frames_match_oracle_samples(config, mode):
-    npy, js = make_golden.golden_paths(config, mode)
-    if not os.path.exists(npy):
-        pytest.skip(f"no stored oracle samples for {config} {mode} (tests/golden/make_golden.py)")
-    meta = json.load(open(js))
     cfg = synthetic.DECODE_CONFIGS[config]
+    batches = [None] if cfg.B == 1 else list(range(cfg.B))
+    paths = [make_golden.golden_paths(config, mode, b) for b in batches]
+    missing = [p for p, _ in paths if not os.path.exists(p)]
+    if missing:
+        pytest.skip(f"no stored oracle samples {missing} (tests/golden/make_golden.py)")
     say("full decode", config, mode)
     z, W = cfg.latents(), cfg.weights()
     video = gpu_decode(z, W, mode)
     assert tuple(video.shape) == (cfg.B, 3, cfg.frames, 16 * cfg.h, 16 * cfg.w)
-    head = video[:, :, :meta["video_shape"][2]]
-    idx = make_golden.sample_index(tuple(meta["video_shape"]))
-    got = to_np(head[tuple(torch.from_numpy(i).to(dev()) for i in idx)])
-    gate(got, np.load(npy), mode, f"{config} {mode} samples")
+    for b, (npy, js) in zip(batches, paths):
+        meta = json.load(open(js))
+        shape = tuple(meta["video_shape"])
+        head = video[:, :, :shape[2]] if b is None else video[b:b + 1, :, :shape[2]]
+        idx = make_golden.sample_index(shape)
+        got = to_np(head[tuple(torch.from_numpy(i).to(dev()) for i in idx)])
+        want = np.load(npy).astype(np.float64)
+        noise = None
+        if mode == "bf16":
+            # the oracle's own decode with float32 sums at the same samples (this batch element's,
+            # else the first element's: the same decoder on equally distributed latents)
+            for nb in (b, 0 if b is not None else None):
+                ref, _ = make_golden.golden_paths(config, mode, nb, acc="f32")
+                if os.path.exists(ref):
+                    noise = np.abs(np.load(ref).astype(np.float64) - (want if nb == b else np.load(
+                        make_golden.golden_paths(config, mode, nb)[0]).astype(np.float64)))
+                    break
+        gate(got, want, mode, f"{config} {mode} batch {b} samples", noise)
     # causality at full size: the first 5 frames are the decode of the first 2 latent frames
     prefix = gpu_decode(np.ascontiguousarray(z[:, :, :2]), W, mode)
-    assert torch.equal(prefix, head)
+    assert torch.equal(prefix, video[:, :, :5])
     assert torch.isfinite(video).all()
     del video, prefix
     torch.cuda.empty_cache()

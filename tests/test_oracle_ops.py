@@ -27,7 +27,14 @@ def rnd(seed, *shape, scale=1.0):
 
 # ------------------------------------------------------------------ bf16 rounding
 
-def test_round_bf16_matches_torch_cast():
+def rne_bf16_bits(x):
+    """Round to nearest even, float32 -> bfloat16, on the bit patterns (reference)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16).astype(np.uint32)
+    return r.view(np.float32)
+
+
+def test_round_bf16_is_round_to_nearest_even():
     g = np.random.default_rng(0)
     x = np.concatenate([
         g.standard_normal(20000).astype(np.float32) * 10.0 ** g.integers(-30, 30, 20000),
@@ -36,9 +43,11 @@ def test_round_bf16_matches_torch_cast():
     # exact ties: the low 16 bits are 0x8000, half way between two bf16 values
     ties = (g.integers(0, 2**15, 4000, dtype=np.uint32) << 16 | 0x8000).astype(np.uint32).view(np.float32)
     x = np.concatenate([x, ties[np.isfinite(ties)]])
-    want = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
     got = oracle.round_bf16(x)
-    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    assert np.array_equal(got.view(np.uint32), rne_bf16_bits(x).view(np.uint32))
+    # ties go to the even neighbour
+    assert oracle.round_bf16(np.array([1.00390625], np.float32))[0] == 1.0          # 1 + 2^-8: tie, even is 1
+    assert oracle.round_bf16(np.array([1.01171875], np.float32))[0] == 1.015625     # 1 + 3*2^-8: tie, even is 1 + 2^-6
     assert np.isnan(oracle.round_bf16(np.array([np.nan], np.float32)))[0]
 
 
