@@ -83,6 +83,8 @@ enum ConvTile {
   kTileDma128x128 = 5,
   kTileDma128x256 = 6,
   kTileDma16x256 = 7,   // bf16, small Cout (conv_out)
+  kTileDma256x256w8 = 8,   // 8 waves, 128 x 64 per wave
+  kTileDma256x256w8b = 9,  // 8 waves, 64 x 128 per wave
 };
 
 hipError_t launch_conv(const ConvArgs& a, int dtype, int tile, hipStream_t s);

@@ -158,7 +158,9 @@ __device__ __forceinline__ void conv_epilogue(const ConvArgs& a, int t, int b, i
 
 // 256 bytes of zeros in device memory: the source of every load that stands for padding,
 // a missing history frame or a channel beyond the tensor (never written).
-static __device__ __attribute__((aligned(256))) uint4 g_zero_page[16];
+// 4 KB: a load that stands for a zero row may also add the row's channel-block offset
+// (at most 2 KB for 1024 channels) to it and still read zeros.
+static __device__ __attribute__((aligned(256))) uint4 g_zero_page[256];
 
 // ------------------------------------------------------------------ implicit-GEMM conv
 //
@@ -432,8 +434,10 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
 }
 
-template <int TC, int TP, int WGC, int WGP, int STAGES, int MINB>
+template <int TC, int TP, int WGC, int WGP, int STAGES, int MINB, bool ALIGNED>
 __global__ void __launch_bounds__(64 * WGC * WGP, MINB) k_conv_dma(const ConvArgs a) {
+  // ALIGNED: Cin % 32 == 0 and Cout % TC == 0, so every weight row of the tile exists and no
+  // 16-byte chunk straddles the end of a pixel: the per-step loads need no selects.
   using T = bf16_t;
   constexpr int NWAVE = WGC * WGP;
   constexpr int ROWB = 64;                       // 32 bf16 per row per step
@@ -455,7 +459,8 @@ __global__ void __launch_bounds__(64 * WGC * WGP, MINB) k_conv_dma(const ConvArg
   __shared__ __attribute__((aligned(1024))) char s2[STAGES > 2 ? STAGE : 16];
   __shared__ __attribute__((aligned(1024))) char s3[STAGES > 3 ? STAGE : 16];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS targets are scalar
   const int HWo = a.Ho * a.Wo;
   const int M = a.F * a.B * HWo;
   const int nct = (a.Cout + TC - 1) / TC;
@@ -472,13 +477,18 @@ __global__ void __launch_bounds__(64 * WGC * WGP, MINB) k_conv_dma(const ConvArg
   // this lane's DMA slots: row r = base + lane / 4, slot lane % 4 holding chunk slot ^ swz
   const int lrow = lane >> 2, lslot = lane & 3;
   const int lchunk = lslot ^ ((lrow >> 1) & 3);
-  // W rows: instruction i covers tile rows (wave * NIW + i) * 16 .. + 15
+  // W rows: instruction i covers tile rows (wave * NIW + i) * 16 .. + 15. Aligned: the byte
+  // offset of this lane's chunk from the tile's first weight row is fixed; a scalar base
+  // advances by the step's K offset.
+  const char* wtile = (const char*)((const T*)a.w + (int64_t)c0 * Ktot);
+  uint32_t woffl[NIW];
   const T* wrow[NIW];
   int wdst[NIW];  // LDS offset of the instruction's 16 rows (the spare slot past the W tile)
 #pragma unroll
   for (int i = 0; i < NIW; ++i) {
     const int r = (wave * NIW + i) * 16;
     const int n = c0 + r + lrow;
+    woffl[i] = (uint32_t)(((int64_t)(r + lrow) * Ktot + lchunk * 8) * 2);
     wrow[i] = (r < TC && n < a.Cout) ? (const T*)a.w + n * Ktot + lchunk * 8 : nullptr;
     wdst[i] = r < TC ? r * ROWB : SW + SA;
   }
@@ -512,8 +522,9 @@ __global__ void __launch_bounds__(64 * WGC * WGP, MINB) k_conv_dma(const ConvArg
   }
 
   // issue cursor: the next K step to load (taps major, 32-channel blocks minor), advanced
-  // without divisions; per tap each A row's pointer to its input pixel (nullptr: zeros)
-  const T* ap[NIA];
+  // without divisions; per tap each A row's source pointer (the zero page where the tap reads
+  // zeros: padding, a missing history frame, a position past the end)
+  const char* ap[NIA];
   int cdt = 0, cdy = 0, cdx = 0, ccs = 0;
   int64_t woff = 0;
   auto set_tap = [&]() {
@@ -532,7 +543,7 @@ __global__ void __launch_bounds__(64 * WGC * WGP, MINB) k_conv_dma(const ConvArg
         xx = rx[i] + cdx - pw;
         ok = ok && yy >= 0 && yy < a.Hin && xx >= 0 && xx < a.Win;
       }
-      ap[i] = ok ? base + ((int64_t)yy * a.Win + xx) * a.Cin + lchunk * 8 : nullptr;
+      ap[i] = ok ? (const char*)(base + ((int64_t)yy * a.Win + xx) * a.Cin + lchunk * 8) : zero + lchunk * 16;
     }
   };
   auto advance = [&]() {
@@ -551,16 +562,27 @@ __global__ void __launch_bounds__(64 * WGC * WGP, MINB) k_conv_dma(const ConvArg
   };
   auto issue = [&](char* buf) {
     const int cb = ccs * 32;
-    const bool cok = cb + lchunk * 8 < a.Cin;
+    if constexpr (ALIGNED) {
+      const char* wstep = wtile + (woff + cb) * 2;
 #pragma unroll
-    for (int i = 0; i < NIW; ++i) {
-      const char* src = (cok && wrow[i]) ? (const char*)(wrow[i] + woff + cb) : zero;
-      __builtin_amdgcn_global_load_lds((const void*)src, LDS_PTR(buf + wdst[i]), 16, 0, 0);
-    }
+      for (int i = 0; i < NIW; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(wstep + woffl[i]), LDS_PTR(buf + wdst[i]), 16, 0, 0);
 #pragma unroll
-    for (int i = 0; i < NIA; ++i) {
-      const char* src = (cok && ap[i]) ? (const char*)(ap[i] + cb) : zero;
-      __builtin_amdgcn_global_load_lds((const void*)src, LDS_PTR(buf + SW + (wave * NIA + i) * 1024), 16, 0, 0);
+      for (int i = 0; i < NIA; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(ap[i] + cb * 2), LDS_PTR(buf + SW + (wave * NIA + i) * 1024), 16,
+                                         0, 0);
+    } else {
+      const bool cok = cb + lchunk * 8 < a.Cin;
+#pragma unroll
+      for (int i = 0; i < NIW; ++i) {
+        const char* src = (cok && wrow[i]) ? (const char*)(wrow[i] + woff + cb) : zero;
+        __builtin_amdgcn_global_load_lds((const void*)src, LDS_PTR(buf + wdst[i]), 16, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < NIA; ++i) {
+        const char* src = cok ? ap[i] + cb * 2 : zero;
+        __builtin_amdgcn_global_load_lds((const void*)src, LDS_PTR(buf + SW + (wave * NIA + i) * 1024), 16, 0, 0);
+      }
     }
     advance();
   };
@@ -576,9 +598,11 @@ __global__ void __launch_bounds__(64 * WGC * WGP, MINB) k_conv_dma(const ConvArg
   auto compute = [&](const char* buf) {
     uint4 wf[TCN], af[TPN];
 #pragma unroll
-    for (int ic = 0; ic < TCN; ++ic) wf[ic] = *(const uint4*)(buf + (wc * WC + ic * 16) * ROWB + rslot);
-#pragma unroll
     for (int ip = 0; ip < TPN; ++ip) af[ip] = *(const uint4*)(buf + SW + (wp * WP + ip * 16) * ROWB + rslot);
+#pragma unroll
+    for (int ic = 0; ic < TCN; ++ic) wf[ic] = *(const uint4*)(buf + (wc * WC + ic * 16) * ROWB + rslot);
+    // all fragment reads are issued before the MFMAs: each MFMA waits only for its own
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ic = 0; ic < TCN; ++ic)
 #pragma unroll
@@ -1071,7 +1095,12 @@ template <int TC, int TP, int WGC, int WGP, int STAGES, int MINB>
 static hipError_t conv_dma_go(const ConvArgs& a, hipStream_t s) {
   const int64_t M = (int64_t)a.F * a.B * a.Ho * a.Wo;
   const int64_t blocks = ((a.Cout + TC - 1) / TC) * ((M + TP - 1) / TP);
-  hipLaunchKernelGGL((k_conv_dma<TC, TP, WGC, WGP, STAGES, MINB>), dim3((unsigned)blocks), dim3(64 * WGC * WGP), 0, s, a);
+  if (a.Cin % 32 == 0 && a.Cout % TC == 0)
+    hipLaunchKernelGGL((k_conv_dma<TC, TP, WGC, WGP, STAGES, MINB, true>), dim3((unsigned)blocks), dim3(64 * WGC * WGP), 0,
+                       s, a);
+  else
+    hipLaunchKernelGGL((k_conv_dma<TC, TP, WGC, WGP, STAGES, MINB, false>), dim3((unsigned)blocks), dim3(64 * WGC * WGP), 0,
+                       s, a);
   return hipGetLastError();
 }
 
@@ -1082,6 +1111,8 @@ hipError_t launch_conv(const ConvArgs& a, int dtype, int tile, hipStream_t s) {
     if (tile == kTileDma128x256) return conv_dma_go<128, 256, 2, 2, 3, 2>(a, s);
     if (tile == kTileDma128x128) return conv_dma_go<128, 128, 2, 2, 4, 2>(a, s);
     if (tile == kTileDma16x256) return conv_dma_go<16, 256, 1, 4, 4, 2>(a, s);
+    if (tile == kTileDma256x256w8) return conv_dma_go<256, 256, 2, 4, 4, 1>(a, s);
+    if (tile == kTileDma256x256w8b) return conv_dma_go<256, 256, 4, 2, 4, 1>(a, s);
     if (tile == kTile32x256) return conv_go<bf16_t, 32, 256>(a, s);
     if (tile == kTile256x128) return conv_go<bf16_t, 256, 128>(a, s);
     return conv_go<bf16_t, 128, 128>(a, s);

@@ -339,9 +339,10 @@ static int pick_tile(int Cout, int64_t M, int mode, int dtype) {
   const bool dma_ok = dtype == kBF16 && mode != kEpiVideo && Cout % 8 == 0 && Cout > 64;
   if (!dma_ok) return Cout <= 64 ? kTile32x256 : kTile128x128;
   if (forced >= 0) return forced;
-  // 256 x 128 tiles (128 x 64 per wave) where there are enough positions to fill the chip;
+  // 256 x 256 tiles (8 waves of 64 x 128) where there are enough positions to fill the chip;
   // 128 x 128 on the level-0 layers (3,520 positions per frame)
-  return M >= 16384 ? kTileDma256x128 : kTileDma128x128;
+  if (M < 16384) return kTileDma128x128;
+  return Cout % 256 == 0 ? kTileDma256x256w8b : kTileDma256x128;
 }
 
 struct ConvCall {
