@@ -151,6 +151,22 @@ int wanvae_attn_block(const void *x, int32_t layout, int64_t B, int64_t C, int64
 int wanvae_profile_enable(int on);
 int wanvae_profile_read(int kind, double *ms, int64_t *launches, double *flops, double *bytes);
 
+/*
+ * Conv kernel selection, for testing and tuning. By default (kernel = -1) each conv takes the
+ * kernel its shape and dtype call for. kernel in 0..WANVAE_CONV_KERNELS-1 asks every later
+ * conv of any thread to use that kernel where it can run the conv (bf16 for kernels 2..10;
+ * kernel 10 only for 3x3 spatial convs with Cin % 32 == 0 and Cout % 128 == 0); other convs
+ * keep the default. The kernels compute the same sums in different orders, so results agree
+ * to rounding, not bit for bit. The environment variable WANVAE_CONV_TILE gives the initial
+ * setting. Returns WANVAE_EARG for a kernel outside -1..WANVAE_CONV_KERNELS-1. Do not change
+ * it while another thread is enqueueing work.
+ *   0: 128 x 128 tile, register-staged loads    1: 32 x 256 (small Cout)
+ *   2: 256 x 128, register-staged                3..9: direct-to-LDS pipelines (bf16)
+ *  10: 3x3 halo tile, 128 channels x 16 x 32 positions, input patch shared by the taps (bf16)
+ */
+#define WANVAE_CONV_KERNELS 11
+int wanvae_set_conv_kernel(int kernel);
+
 /* Message for the last failed call on this thread ("" if none). Valid until the next call. */
 const char *wanvae_last_error(void);
 

@@ -127,10 +127,13 @@ class DecodeConfig:
         return gen_weights(self.base, self.seed, self.bias_std)
 
 
-# The decode workloads. tiny: decoder_base_dim 16, 2 latent frames of 4x4.
+# The decode workloads. tiny: decoder_base_dim 16, 2 latent frames of 4x4. small32:
+# decoder_base_dim 32 (128-channel levels, the width the 3x3 halo-tile conv kernel needs),
+# 2 latent frames of 8x12 (5 video frames of 128x192).
 # ti2v5b_*: decoder_base_dim 256 at 704x1280 (landscape) or 1280x704 (portrait), 31 latent frames.
 DECODE_CONFIGS = {
     "tiny": DecodeConfig("tiny", 16, 1, 2, 4, 4, 0, 0.1),
+    "small32": DecodeConfig("small32", 32, 1, 2, 8, 12, 5, 0.1),
     "ti2v5b_landscape": DecodeConfig("ti2v5b_landscape", 256, 1, 31, 44, 80, 3, None),
     "ti2v5b_portrait": DecodeConfig("ti2v5b_portrait", 256, 1, 31, 80, 44, 4, None),
     "ti2v5b_landscape_b2": DecodeConfig("ti2v5b_landscape_b2", 256, 2, 31, 44, 80, 4, None),

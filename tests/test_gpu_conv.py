@@ -29,6 +29,14 @@ SMALL = [
 ]
 
 
+# bf16 convs the halo-tile kernel takes by default (3x3, Cin % 32 == 0, Cout % 128 == 0, frames
+# of at least 32 x 64, at least 16,384 positions): ragged 16 x 32 blocks, batch 2, a 2-D conv
+HALO = [
+    (32, 128, 3, 3, 3, 2, 40, 210, 2, 2),
+    (64, 256, 1, 3, 3, 1, 70, 120, 0, 2),
+]
+
+
 def run_gpu(x, cache, w, b, mode, layout):
     xt, wt, bt = to_dev(x, mode), to_dev(w, mode), to_dev(b, mode)
     ct = to_dev(cache, mode) if cache is not None and cache.shape[2] else None
@@ -56,19 +64,53 @@ def check(got, x, cache, w, b, mode, what):
         assert_bf16_close(got, want, err, what=what)
 
 
-@pytest.mark.parametrize("mode", ["fp32", "bf16"])
-@pytest.mark.parametrize("layout", ["ncthw", "nthwc"])
-@pytest.mark.parametrize("case", SMALL)
-def test_conv_small(case, layout, mode):
+def inputs(case):
     Ci, Co, kt, kh, kw, t, h, w, nc, B = case
-    say("conv", case, layout, mode)
     g = np.random.default_rng(abs(hash(case)) % 2**31)
     x = g.standard_normal((B, Ci, t, h, w)).astype(np.float32)
     cache = g.standard_normal((B, Ci, nc, h, w)).astype(np.float32) if nc else None
     wgt = (g.standard_normal((Co, Ci, kt, kh, kw)) / np.sqrt(Ci * kt * kh * kw)).astype(np.float32)
     b = (0.1 * g.standard_normal(Co)).astype(np.float32)
+    return x, cache, wgt, b
+
+
+@pytest.mark.parametrize("mode", ["fp32", "bf16"])
+@pytest.mark.parametrize("layout", ["ncthw", "nthwc"])
+@pytest.mark.parametrize("case", SMALL)
+def test_conv_small(case, layout, mode):
+    say("conv", case, layout, mode)
+    x, cache, wgt, b = inputs(case)
     got = run_gpu(x, cache, wgt, b, mode, layout)
     check(got, x, cache, wgt, b, mode, f"{case} {layout} {mode}")
+
+
+@pytest.mark.parametrize("layout", ["ncthw", "nthwc"])
+@pytest.mark.parametrize("case", HALO)
+def test_conv_halo_tile_default(case, layout):
+    say("conv", case, layout, "bf16")
+    x, cache, wgt, b = inputs(case)
+    got = run_gpu(x, cache, wgt, b, "bf16", layout)
+    check(got, x, cache, wgt, b, "bf16", f"{case} {layout} bf16")
+
+
+@pytest.fixture
+def conv_kernel():
+    try:
+        yield wanvae.wanvae_set_conv_kernel
+    finally:
+        wanvae.wanvae_set_conv_kernel(-1)
+
+
+@pytest.mark.parametrize("kernel", range(wanvae.CONV_KERNELS))
+@pytest.mark.parametrize("case", SMALL + HALO[:1])
+def test_conv_each_kernel_bf16(case, kernel, conv_kernel):
+    """Every conv kernel, forced wherever it can run the conv, against the oracle."""
+    say("conv", case, "kernel", kernel)
+    conv_kernel(kernel)
+    x, cache, wgt, b = inputs(case)
+    got = run_gpu(x, cache, wgt, b, "bf16", "nthwc")
+    check(got, x, cache, wgt, b, "bf16", f"{case} kernel {kernel}")
+
 
 
 def test_conv_is_deterministic_and_zero_history_equals_no_history():

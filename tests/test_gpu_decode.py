@@ -63,6 +63,37 @@ def oracle_with_noise(z, W, mode):
     return want, np.abs(oracle.decode(z, W, mode, acc="f32").astype(np.float64) - want)
 
 
+@pytest.fixture
+def conv_kernel():
+    """Sets the conv kernel for one test and restores the default afterwards."""
+    try:
+        yield wanvae.wanvae_set_conv_kernel
+    finally:
+        wanvae.wanvae_set_conv_kernel(-1)
+
+
+@pytest.fixture(scope="module")
+def small32():
+    cfg = synthetic.DECODE_CONFIGS["small32"]
+    z, W = cfg.latents(), cfg.weights()
+    say("small32 oracle (f64 and f32 sums)")
+    want, noise = oracle_with_noise(z, W, "bf16")
+    return z, W, want, noise
+
+
+@pytest.mark.parametrize("kernel", [-1, 10, 9, 5, 3])
+def test_small32_bf16_decode_each_conv_kernel(small32, conv_kernel, kernel):
+    """decoder_base_dim 32: every 3x3 conv of the 128-channel levels, the upsampling ones
+    included, runs on the forced kernel (10: the halo tile) with the residual and DupUp3D
+    epilogues; the whole decode is checked against the oracle."""
+    z, W, want, noise = small32
+    conv_kernel(kernel)
+    say("small32 bf16 decode, conv kernel", kernel)
+    got = to_np(gpu_decode(z, W, "bf16"))
+    assert got.shape == want.shape == (1, 3, 5, 128, 192)
+    gate(got, want, "bf16", f"small32 kernel {kernel}", noise)
+
+
 @pytest.fixture(scope="module")
 def tiny():
     cfg = synthetic.DECODE_CONFIGS["tiny"]

@@ -162,3 +162,14 @@ def test_conv_and_attention_validation():
     assert attn(C=96) == W.ESHAPE
     assert attn(y=4096) == W.EARG
     assert attn(gam=W.tensor_struct("gamma", torch.zeros(63))) == W.ESHAPE
+
+
+def test_conv_kernel_selection_range():
+    try:
+        for k in range(-1, W.CONV_KERNELS):
+            W.wanvae_set_conv_kernel(k)
+        for bad in (-2, W.CONV_KERNELS):
+            with pytest.raises(ValueError):
+                W.wanvae_set_conv_kernel(bad)
+    finally:
+        W.wanvae_set_conv_kernel(-1)

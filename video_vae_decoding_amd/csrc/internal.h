@@ -85,9 +85,12 @@ enum ConvTile {
   kTileDma16x256 = 7,   // bf16, small Cout (conv_out)
   kTileDma256x256w8 = 8,   // 8 waves, 128 x 64 per wave
   kTileDma256x256w8b = 9,  // 8 waves, 64 x 128 per wave
+  kTileHalo128x16x32 = 10, // bf16 3x3 convs: 128 channels x a 16 x 32 block, input patch reused over the taps
 };
 
 hipError_t launch_conv(const ConvArgs& a, int dtype, int tile, hipStream_t s);
+// whether the halo-tile kernel handles this conv (bf16, 3x3 spatial, Cin % 32, Cout % 128, frame epilogue)
+bool conv_halo_supported(const ConvArgs& a, int dtype, int tile);
 hipError_t launch_norm(const NormArgs& a, int dtype, hipStream_t s);
 bool attn_supported(int C, int dtype);
 hipError_t launch_attn(const AttnArgs& a, int dtype, hipStream_t s);

@@ -434,10 +434,11 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
 }
 
-template <int TC, int TP, int WGC, int WGP, int STAGES, int MINB, bool ALIGNED>
+template <int TC, int TP, int WGC, int WGP, int STAGES, int MINB, bool ALIGNED, bool RB2 = false>
 __global__ void __launch_bounds__(64 * WGC * WGP, MINB) k_conv_dma(const ConvArgs a) {
-  // ALIGNED: Cin % 32 == 0 and Cout % TC == 0, so every weight row of the tile exists and no
-  // 16-byte chunk straddles the end of a pixel: the per-step loads need no selects.
+  // ALIGNED: Cin % 32 == 0, Cout % TC == 0 and TC >= 16 * waves, so every weight row a wave
+  // loads exists and no 16-byte chunk straddles the end of a pixel: the per-step loads need
+  // no selects.
   using T = bf16_t;
   constexpr int NWAVE = WGC * WGP;
   constexpr int ROWB = 64;                       // 32 bf16 per row per step
@@ -453,6 +454,7 @@ __global__ void __launch_bounds__(64 * WGC * WGP, MINB) k_conv_dma(const ConvArg
   constexpr int SW = TC * ROWB, SA = TP * ROWB, STAGE = SW + SA + SPARE;
   static_assert((TC < 16 * NWAVE || NIW * 16 * NWAVE == TC) && NIA * 16 * NWAVE == TP, "tile / wave mismatch");
   static_assert(TC % 16 == 0, "W tile rows");
+  static_assert(!ALIGNED || TC >= 16 * NWAVE, "the aligned path has no spare weight rows");
   static_assert(STAGES >= 2 && STAGES <= 4, "stages");
   __shared__ __attribute__((aligned(1024))) char s0[STAGE];
   __shared__ __attribute__((aligned(1024))) char s1[STAGE];
@@ -595,38 +597,122 @@ __global__ void __launch_bounds__(64 * WGC * WGP, MINB) k_conv_dma(const ConvArg
     for (int ip = 0; ip < TPN; ++ip) acc[ic][ip] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   // fragment reads: row base + (lane & 15), logical chunk lane >> 4
   const int rslot = ((lane >> 4) ^ (((lane & 15) >> 1) & 3)) * 16 + (lane & 15) * ROWB;
-  auto compute = [&](const char* buf) {
-    uint4 wf[TCN], af[TPN];
-#pragma unroll
-    for (int ip = 0; ip < TPN; ++ip) af[ip] = *(const uint4*)(buf + SW + (wp * WP + ip * 16) * ROWB + rslot);
-#pragma unroll
-    for (int ic = 0; ic < TCN; ++ic) wf[ic] = *(const uint4*)(buf + (wc * WC + ic * 16) * ROWB + rslot);
-    // all fragment reads are issued before the MFMAs: each MFMA waits only for its own
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int ic = 0; ic < TCN; ++ic)
-#pragma unroll
-      for (int ip = 0; ip < TPN; ++ip) Mma<T>::run(acc[ic][ip], wf[ic], af[ip]);
+  // waits until this wave's loads of step s are done (at most the later steps' pending) and
+  // its LDS reads have returned, then the workgroup barrier: step s's tile is complete in LDS
+  // for every wave, and every wave is done reading the buffers of the steps before s - 1
+  auto sync_step = [&](int s) {
+    if (s + STAGES - 2 < steps)
+      wait_vm_lgkm0<NI * (STAGES - 2)>();
+    else
+      wait_vm_lgkm0<0>();
+    __builtin_amdgcn_s_barrier();
   };
   char* bufs[4] = {s0, s1, s2, s3};
-
-  set_tap();
+  if constexpr (RB2) {
+    // One wave per SIMD: two register sets of fragments. The MFMAs of step s (set s & 1)
+    // are interleaved with the LDS reads of step s + 1 into the other set, so the read
+    // latency hides behind the matrix pipe without a second wave. The barrier of step s + 1
+    // comes first: after it, no wave reads the buffer of step s any more (its fragments are
+    // in registers), and the DMA of step s + STAGES refills it.
+    uint4 wf[2][TCN], af[2][TPN];
+    auto rd = [&](int set, const char* buf) {
 #pragma unroll
-  for (int p = 0; p < STAGES - 1; ++p)
-    if (p < steps) issue(bufs[p]);
-  for (int sb = 0; sb < steps; sb += STAGES) {
+      for (int ic = 0; ic < TCN; ++ic) wf[set][ic] = *(const uint4*)(buf + (wc * WC + ic * 16) * ROWB + rslot);
 #pragma unroll
-    for (int u = 0; u < STAGES; ++u) {
-      const int s = sb + u;
-      if (s < steps) {
-        // this wave's loads of step s are done once at most the later steps' are pending
-        if (s + STAGES - 2 < steps)
-          wait_vm_lgkm0<NI * (STAGES - 2)>();
-        else
-          wait_vm_lgkm0<0>();
-        __builtin_amdgcn_s_barrier();
-        if (s + STAGES - 1 < steps) issue(bufs[(u + STAGES - 1) % STAGES]);
-        compute(bufs[u]);
+      for (int ip = 0; ip < TPN; ++ip) af[set][ip] = *(const uint4*)(buf + SW + (wp * WP + ip * 16) * ROWB + rslot);
+    };
+    set_tap();
+#pragma unroll
+    for (int p = 0; p < STAGES - 1; ++p)
+      if (p < steps) issue(bufs[p]);
+    sync_step(0);
+    if (STAGES - 1 < steps) issue(bufs[STAGES - 1]);
+    rd(0, bufs[0]);
+    static_assert(STAGES % 2 == 0, "register sets alternate with the stage buffers");
+    auto mfma = [&](int set) {
+#pragma unroll
+      for (int ip = 0; ip < TPN; ++ip)
+#pragma unroll
+        for (int ic = 0; ic < TCN; ++ic) Mma<T>::run(acc[ic][ip], wf[set][ic], af[set][ip]);
+    };
+    // each step: barrier of s + 1 and the refill, then the reads of s + 1 and the MFMAs of s
+    // in one basic block, one read between groups of MFMAs. The last step reads a stale
+    // buffer into the idle set (no DMA is in flight by then) so that its block is the same.
+    for (int sb = 0; sb < steps; sb += STAGES) {
+#pragma unroll
+      for (int u = 0; u < STAGES; ++u) {
+        const int s = sb + u, cur = u & 1;
+        if (s < steps) {
+          if (s + 1 < steps) {
+            sync_step(s + 1);
+            if (s + STAGES < steps) issue(bufs[u]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          rd(cur ^ 1, bufs[(u + 1) % STAGES]);
+          mfma(cur);
+#pragma unroll
+          for (int g = 0; g < TCN + TPN; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, (TCN * TPN) / (TCN + TPN), 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+  } else {
+    constexpr int H = TPN / 2;  // the step's MFMAs run in two halves of position fragments
+    static_assert(TPN % 2 == 0, "two halves");
+    uint4 wf[TCN], af[TPN], an[H];
+    auto read_w = [&](const char* buf) {
+#pragma unroll
+      for (int ic = 0; ic < TCN; ++ic) wf[ic] = *(const uint4*)(buf + (wc * WC + ic * 16) * ROWB + rslot);
+    };
+    auto read_a = [&](const char* buf, int ip0, uint4* dst) {
+#pragma unroll
+      for (int k = 0; k < H; ++k) dst[k] = *(const uint4*)(buf + SW + (wp * WP + (ip0 + k) * 16) * ROWB + rslot);
+    };
+    auto mfma_half = [&](int ip0) {
+#pragma unroll
+      for (int k = 0; k < H; ++k)
+#pragma unroll
+        for (int ic = 0; ic < TCN; ++ic) Mma<T>::run(acc[ic][ip0 + k], wf[ic], af[ip0 + k]);
+    };
+    // Two waves per SIMD. The barrier of step s+1 sits between the two halves of step s's
+    // MFMAs, so the barrier and the first LDS reads of step s+1 overlap the second half.
+    // After the barrier of step k, the DMA of step k + STAGES - 1 refills the buffer of step
+    // k - 1, whose reads every wave has completed.
+    set_tap();
+#pragma unroll
+    for (int p = 0; p < STAGES - 1; ++p)
+      if (p < steps) issue(bufs[p]);
+    sync_step(0);
+    if (STAGES - 1 < steps) issue(bufs[STAGES - 1]);
+    read_w(bufs[0]);
+    read_a(bufs[0], 0, af);
+    read_a(bufs[0], H, af + H);
+    for (int sb = 0; sb < steps; sb += STAGES) {
+#pragma unroll
+      for (int u = 0; u < STAGES; ++u) {
+        const int s = sb + u;
+        if (s < steps) {
+          mfma_half(0);
+          __builtin_amdgcn_sched_barrier(0);
+          const bool more = s + 1 < steps;
+          if (more) {
+            sync_step(s + 1);
+            if (s + STAGES < steps) issue(bufs[u]);
+            read_a(bufs[(u + 1) % STAGES], 0, an);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          mfma_half(H);
+          __builtin_amdgcn_sched_barrier(0);
+          if (more) {
+            read_w(bufs[(u + 1) % STAGES]);
+            read_a(bufs[(u + 1) % STAGES], H, af + H);
+#pragma unroll
+            for (int k = 0; k < H; ++k) af[k] = an[k];
+          }
+        }
       }
     }
   }
@@ -711,6 +797,278 @@ __global__ void __launch_bounds__(64 * WGC * WGP, MINB) k_conv_dma(const ConvArg
           b = 0;
           ++t;
         }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ 3x3 conv with a halo tile (bf16)
+//
+// For the kh = kw = 3 convs the workgroup owns a 2-D block of TPY x TPX output positions of
+// one frame and TC output channels. For each (time tap, 32-channel block) it copies the input
+// patch under the block, with its one-pixel border, into LDS once (direct-to-LDS loads); the
+// nine spatial taps then read shifted windows of that patch, so the input passes the address
+// units once per patch instead of once per tap. Only the weight tile (TC rows of one tap)
+// streams per step, through a ring of nine LDS buffers (one per spatial tap). With UP the conv
+// reads the nearest x2 upsampling of its input: the patch is the low-resolution region and
+// two neighbouring output positions read the same pixel.
+//
+// Patch pixels are 64-byte rows of 4 chunks stored at slot chunk ^ ((column >> 2) & 3): 16
+// positions along a row hit distinct banks for any shift, and a shift by whole patch rows
+// keeps the permutation, so every fragment address is a per-lane base (one per column shift
+// and 16-column group) plus a compile-time offset.
+
+// a wave-uniform pointer held in scalar registers (buffer descriptors must be scalar)
+__device__ __forceinline__ const char* scalar_ptr(const void* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const char*)(((uint64_t)hi << 32) | lo);
+}
+
+// 16 bytes per lane from base + voff + soff into LDS at lds + 16 * lane (buffer load with
+// an LDS destination): a lane whose voff + soff is not below `bytes` receives zeros.
+__device__ __forceinline__ void buffer_lds16(const char* base, uint32_t bytes, char* lds, uint32_t voff, int soff) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LDS_PTR(lds), 16, voff, soff, 0, 0);
+}
+
+template <int TC, int TPY, int TPX, int WGC, int WGP, bool UP>
+__global__ void __launch_bounds__(64 * WGC * WGP, 1) k_conv_halo(const ConvArgs a) {
+  using T = bf16_t;
+  constexpr int NWAVE = WGC * WGP, NT = 64 * NWAVE;
+  constexpr int TP = TPY * TPX;
+  constexpr int WC = TC / WGC, WP = TP / WGP, TCN = WC / 16, TPN = WP / 16;
+  constexpr int RW = WP / TPX;  // tile rows per wave
+  static_assert(WP % TPX == 0 && TPX % 16 == 0, "each wave holds whole tile rows");
+  static_assert(!UP || (RW % 2 == 0 && TPY % 2 == 0), "upsampled rows pair up");
+  constexpr int PH = UP ? TPY / 2 + 2 : TPY + 2, PW = UP ? TPX / 2 + 2 : TPX + 2;
+  constexpr int P = PH * PW;
+  constexpr int NPI = (P + 15) / 16;                  // patch DMA instructions (16 pixels each)
+  constexpr int NPW = (NPI + NWAVE - 1) / NWAVE;      // per wave (the spare ones load zeros)
+  constexpr int RB = TC * 2;                          // epilogue staging row (bf16 channels)
+  // a patch buffer also holds a quarter of the C tile for the epilogue
+  constexpr int PBUF = NPW * NWAVE * 1024 > TP / 4 * RB ? NPW * NWAVE * 1024 : TP / 4 * RB;
+  constexpr int NIW = TC / (16 * NWAVE);              // weight DMA instructions per wave per step
+  static_assert(NIW >= 1 && NIW * 16 * NWAVE == TC, "weight rows per wave");
+  constexpr int WBUF = TC * 64;
+  constexpr int RPA = PBUF / RB;
+  static_assert(2 * RPA >= TP / 2, "half the C tile fits the patch buffers");
+  __shared__ __attribute__((aligned(1024))) char p0[PBUF];
+  __shared__ __attribute__((aligned(1024))) char p1[PBUF];
+  __shared__ __attribute__((aligned(1024))) char w0[WBUF];
+  __shared__ __attribute__((aligned(1024))) char w1[WBUF];
+  __shared__ __attribute__((aligned(1024))) char w2[WBUF];
+  __shared__ __attribute__((aligned(1024))) char w3[WBUF];
+  __shared__ __attribute__((aligned(1024))) char w4[WBUF];
+  __shared__ __attribute__((aligned(1024))) char w5[WBUF];
+  __shared__ __attribute__((aligned(1024))) char w6[WBUF];
+  __shared__ __attribute__((aligned(1024))) char w7[WBUF];
+  __shared__ __attribute__((aligned(1024))) char w8[WBUF];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nct = a.Cout / TC;
+  const int tiles_x = (a.Wo + TPX - 1) / TPX, tiles_y = (a.Ho + TPY - 1) / TPY;
+  // block coordinates are wave-uniform: keep them scalar so that the frame tables are read
+  // with scalar loads
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int ct = __builtin_amdgcn_readfirstlane(bid % nct);
+  int rem = __builtin_amdgcn_readfirstlane(bid / nct);
+  const int tx = __builtin_amdgcn_readfirstlane(rem % tiles_x);
+  rem = __builtin_amdgcn_readfirstlane(rem / tiles_x);
+  const int ty = __builtin_amdgcn_readfirstlane(rem % tiles_y);
+  rem = __builtin_amdgcn_readfirstlane(rem / tiles_y);
+  const int b = __builtin_amdgcn_readfirstlane(rem % a.B), t = __builtin_amdgcn_readfirstlane(rem / a.B);
+  const int c0 = ct * TC, Y0 = ty * TPY, X0 = tx * TPX;
+  const int csteps = a.Cin / 32;
+  const int G = a.kt * csteps;  // step groups: (time tap, channel block), nine spatial taps each
+  const int S = 9 * G;
+  const int64_t Ktot = (int64_t)a.kt * 9 * a.Cin;
+  const char* zero = (const char*)g_zero_page;
+  const int lrow = lane >> 2, lslot = lane & 3;
+
+  // The copies are buffer loads into LDS: a 32-bit per-lane offset against a descriptor in
+  // scalar registers. A lane whose offset is past the descriptor's size receives zeros (the
+  // padding around the frame, a missing history frame).
+  const int Cin = a.Cin, kt = a.kt;
+  constexpr uint32_t kOut = 0x80000000u;  // offset beyond every descriptor: zeros
+  // weight DMA: as in k_conv_dma (rows of 64 bytes, slot = chunk ^ ((row >> 1) & 3))
+  const int lchunk = lslot ^ ((lrow >> 1) & 3);
+  const char* wbase = scalar_ptr((const T*)a.w + (int64_t)c0 * Ktot);
+  const uint32_t wbytes = (uint32_t)(TC * Ktot * 2);
+  uint32_t woffl[NIW];
+#pragma unroll
+  for (int i = 0; i < NIW; ++i) woffl[i] = (uint32_t)((((wave * NIW + i) * 16 + lrow) * Ktot + lchunk * 8) * 2);
+
+  // patch DMA: instruction i of this wave fills pixels (i * NWAVE + wave) * 16 + lane / 4
+  const int oy = UP ? (Y0 >> 1) - 1 : Y0 - 1, ox = UP ? (X0 >> 1) - 1 : X0 - 1;
+  uint32_t poff[NPW];
+#pragma unroll
+  for (int i = 0; i < NPW; ++i) {
+    const int q = (i * NWAVE + wave) * 16 + lrow;
+    const int prow = q / PW, pcol = q - prow * PW;
+    const int iy = oy + prow, ix = ox + pcol;
+    const bool ok = q < P && iy >= 0 && iy < a.Hin && ix >= 0 && ix < a.Win;
+    poff[i] = ok ? (uint32_t)(((iy * a.Win + ix) * Cin + (lslot ^ ((pcol >> 2) & 3)) * 8) * 2) : kOut;
+  }
+  const uint32_t fbytes = (uint32_t)a.Hin * a.Win * Cin * 2;
+  const char* fb0 = nullptr;
+  const char* fb1 = nullptr;
+  const char* fb2 = nullptr;
+  if (a.in[t]) fb0 = scalar_ptr((const T*)a.in[t] + b * a.in_bs[t]);
+  if (kt > 1) {
+    if (a.in[t + 1]) fb1 = scalar_ptr((const T*)a.in[t + 1] + b * a.in_bs[t + 1]);
+    if (a.in[t + 2]) fb2 = scalar_ptr((const T*)a.in[t + 2] + b * a.in_bs[t + 2]);
+  }
+
+  // wofs: byte offset of a group's first tap in a weight row; a patch is (frame base, channel
+  // byte offset). Groups advance without divisions: channel block minor, time tap major.
+  auto issue_w = [&](char* buf, int wofs, int j) {
+    const int so = wofs + j * Cin * 2;
+#pragma unroll
+    for (int i = 0; i < NIW; ++i)
+      buffer_lds16(wbase, wbytes, buf + (wave * NIW + i) * 1024, woffl[i], so);
+  };
+  // a null base (a missing history frame, or past the last group) loads zeros, so that every
+  // wave keeps the same count of loads in flight
+  auto issue_p = [&](char* buf, const char* base, int cb2) {
+    const char* pbase = scalar_ptr(base != nullptr ? base + cb2 : zero);
+    const uint32_t pbytes = base != nullptr ? fbytes : 0u;
+#pragma unroll
+    for (int i = 0; i < NPW; ++i) buffer_lds16(pbase, pbytes, buf + (i * NWAVE + wave) * 1024, poff[i], 0);
+  };
+  // cursor: (time tap, channel block) of the group after the current one, and its frame
+  int ndt = 0, ncb = 0;
+  const char* nfb = fb0;
+  auto advance = [&]() {
+    ncb += 32;
+    if (ncb == Cin) {
+      ncb = 0;
+      ++ndt;
+      nfb = ndt == 1 ? fb1 : (ndt == 2 ? fb2 : nullptr);  // past the last time tap: zeros
+    }
+  };
+  auto nwofs = [&]() -> int { return (ndt * 9 * Cin + ncb) * 2; };
+
+  const int wc = wave / WGP, wp = wave % WGP;
+  f32x4_t acc[TCN][TPN];
+#pragma unroll
+  for (int ic = 0; ic < TCN; ++ic)
+#pragma unroll
+    for (int ip = 0; ip < TPN; ++ip) acc[ic][ip] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // weight fragments: row base + (lane & 15), logical chunk lane >> 4
+  const int wrd = (wc * WC + (lane & 15)) * 64 + ((lane >> 4) ^ (((lane & 15) >> 1) & 3)) * 16;
+  // patch fragment bases, per 16-column group and column shift dx
+  constexpr int NXG = TPX / 16;
+  int pvb[NXG][3];
+#pragma unroll
+  for (int xg = 0; xg < NXG; ++xg)
+#pragma unroll
+    for (int dx = 0; dx < 3; ++dx) {
+      const int px = xg * 16 + (lane & 15);
+      const int col = UP ? ((px + dx - 1) >> 1) + 1 : px + dx;
+      const int wrow = UP ? wp * (RW / 2) : wp * RW;
+      pvb[xg][dx] = (wrow * PW + col) * 64 + (((lane >> 4) ^ ((col >> 2) & 3)) << 4);
+    }
+
+  char* wb[9] = {w0, w1, w2, w3, w4, w5, w6, w7, w8};
+  issue_p(p0, fb0, 0);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) issue_w(wb[j], 0, j);
+  int cur_wofs = 0;
+  advance();  // the cursor names group 1
+
+  for (int g0 = 0; g0 < G; g0 += 2) {
+#pragma unroll
+    for (int gg = 0; gg < 2; ++gg) {
+      const int g = g0 + gg;
+      if (g < G) {
+        char* pcur = gg == 0 ? p0 : p1;
+        char* pnext = gg == 0 ? p1 : p0;
+        const int next_wofs = nwofs();
+#pragma unroll
+        for (int j = 0; j < 9; ++j) {
+          const int s = 9 * g + j;
+          // this wave's loads of step s (and of the group's patch, issued earlier) have landed
+          if (s + 7 < S) {
+            if (j == 0)
+              wait_vm_lgkm0<7 * NIW>();
+            else
+              wait_vm_lgkm0<7 * NIW + NPW>();
+          } else {
+            wait_vm_lgkm0<0>();
+          }
+          __builtin_amdgcn_s_barrier();
+          // refill the buffer of step s - 1 with step s + 8; at a group's first step, the
+          // patch of the next group goes to the buffer the previous group used
+          if (s + 8 < S) issue_w(wb[(j + 8) % 9], j == 0 ? cur_wofs : next_wofs, (j + 8) % 9);
+          if (j == 0) issue_p(pnext, nfb, ncb * 2);
+          __builtin_amdgcn_sched_barrier(0);
+          const int dy = j / 3, dx = j % 3;
+          uint4 wf[TCN], bf[TPN];
+#pragma unroll
+          for (int ic = 0; ic < TCN; ++ic) wf[ic] = *(const uint4*)(wb[j] + wrd + ic * 16 * 64);
+#pragma unroll
+          for (int ip = 0; ip < TPN; ++ip) {
+            const int k = (ip * 16) / TPX, xg = ((ip * 16) % TPX) / 16;
+            const int rowc = UP ? ((k + dy - 1) >> 1) + 1 : k + dy;
+            bf[ip] = *(const uint4*)(pcur + pvb[xg][dx] + rowc * PW * 64);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int ip = 0; ip < TPN; ++ip)
+#pragma unroll
+            for (int ic = 0; ic < TCN; ++ic) Mma<T>::run(acc[ic][ip], wf[ic], bf[ip]);
+        }
+        cur_wofs = next_wofs;
+        advance();
+      }
+    }
+  }
+
+  // Epilogue in two passes of half the positions, staged in the patch buffers (rows of TC
+  // bf16 channels, 8-byte slots permuted by slot ^ (row & 15)); 8-channel units are then
+  // finished and stored with 16-byte accesses.
+  wait_vm_lgkm0<0>();
+  constexpr int SWZ = TC / 4 - 1 < 15 ? TC / 4 - 1 : 15;
+  auto crow = [&](int r) -> char* { return r < RPA ? p0 + r * RB : p1 + (r - RPA) * RB; };
+  float4 bias[TCN];
+#pragma unroll
+  for (int ic = 0; ic < TCN; ++ic) bias[ic] = *(const float4*)(a.bias + c0 + wc * WC + ic * 16 + 4 * (lane >> 4));
+  constexpr int UPR = TC / 8;
+  static_assert(NT % UPR == 0, "units per row divide the workgroup");
+  constexpr int PSTEP = NT / UPR;
+  const int cu = tid % UPR;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    __syncthreads();
+    if (wp / (WGP / 2) == h) {
+#pragma unroll
+      for (int ip = 0; ip < TPN; ++ip) {
+        const int r = (wp - h * (WGP / 2)) * WP + ip * 16 + (lane & 15);
+        char* row = crow(r);
+#pragma unroll
+        for (int ic = 0; ic < TCN; ++ic) {
+          const int c = wc * WC + ic * 16 + 4 * (lane >> 4);
+          uint2 pk;
+          pk.x = pack2_bf16(acc[ic][ip][0] + bias[ic].x, acc[ic][ip][1] + bias[ic].y);
+          pk.y = pack2_bf16(acc[ic][ip][2] + bias[ic].z, acc[ic][ip][3] + bias[ic].w);
+          *(uint2*)(row + (((c >> 2) ^ (r & SWZ)) << 3)) = pk;
+        }
+      }
+    }
+    __syncthreads();
+    for (int r = tid / UPR; r < TP / 2; r += PSTEP) {
+      const int p = h * (TP / 2) + r;
+      const int y = Y0 + p / TPX, x = X0 + p % TPX;
+      if (y < a.Ho && x < a.Wo) {
+        const char* row = crow(r);
+        const uint2 lo = *(const uint2*)(row + (((2 * cu) ^ (r & SWZ)) << 3));
+        const uint2 hi = *(const uint2*)(row + (((2 * cu + 1) ^ (r & SWZ)) << 3));
+        float v[8];
+        unpack8_bf16(make_uint4(lo.x, lo.y, hi.x, hi.y), v);
+        epilogue8_bf16(a, t, b, y, x, c0 + cu * 8, v);
       }
     }
   }
@@ -1091,23 +1449,51 @@ static hipError_t conv_go(const ConvArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int TC, int TP, int WGC, int WGP, int STAGES, int MINB>
+template <int TC, int TP, int WGC, int WGP, int STAGES, int MINB, bool RB2 = false>
 static hipError_t conv_dma_go(const ConvArgs& a, hipStream_t s) {
   const int64_t M = (int64_t)a.F * a.B * a.Ho * a.Wo;
   const int64_t blocks = ((a.Cout + TC - 1) / TC) * ((M + TP - 1) / TP);
-  if (a.Cin % 32 == 0 && a.Cout % TC == 0)
-    hipLaunchKernelGGL((k_conv_dma<TC, TP, WGC, WGP, STAGES, MINB, true>), dim3((unsigned)blocks), dim3(64 * WGC * WGP), 0,
-                       s, a);
-  else
-    hipLaunchKernelGGL((k_conv_dma<TC, TP, WGC, WGP, STAGES, MINB, false>), dim3((unsigned)blocks), dim3(64 * WGC * WGP), 0,
-                       s, a);
+  // the aligned path loads every wave's weight rows unconditionally: only where they all lie
+  // in the tile (16 rows per wave and instruction), not on the 16-channel tile
+  if constexpr (TC >= 16 * WGC * WGP) {
+    if (a.Cin % 32 == 0 && a.Cout % TC == 0) {
+      hipLaunchKernelGGL((k_conv_dma<TC, TP, WGC, WGP, STAGES, MINB, true, RB2>), dim3((unsigned)blocks),
+                         dim3(64 * WGC * WGP), 0, s, a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((k_conv_dma<TC, TP, WGC, WGP, STAGES, MINB, false, RB2>), dim3((unsigned)blocks),
+                     dim3(64 * WGC * WGP), 0, s, a);
   return hipGetLastError();
 }
 
+template <int TC, int TPY, int TPX, int WGC, int WGP>
+static hipError_t conv_halo_go(const ConvArgs& a, hipStream_t s) {
+  const int64_t blocks = (int64_t)(a.Cout / TC) * ((a.Wo + TPX - 1) / TPX) * ((a.Ho + TPY - 1) / TPY) * a.F * a.B;
+  if (a.up)
+    hipLaunchKernelGGL((k_conv_halo<TC, TPY, TPX, WGC, WGP, true>), dim3((unsigned)blocks), dim3(64 * WGC * WGP), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_conv_halo<TC, TPY, TPX, WGC, WGP, false>), dim3((unsigned)blocks), dim3(64 * WGC * WGP), 0, s, a);
+  return hipGetLastError();
+}
+
+bool conv_halo_supported(const ConvArgs& a, int dtype, int tile) {
+  const int TC = 128;
+  (void)tile;
+  return dtype == kBF16 && a.kh == 3 && a.kw == 3 && (a.kt == 1 || a.kt == 3) && a.Cin % 32 == 0 &&
+         a.Cout % TC == 0 && a.mode == kEpiFrames && (!a.up || (a.Ho % 2 == 0 && a.Wo % 2 == 0 && a.Hin * 2 == a.Ho &&
+                                                                a.Win * 2 == a.Wo)) &&
+         (a.up || (a.Hin == a.Ho && a.Win == a.Wo));
+}
+
 hipError_t launch_conv(const ConvArgs& a, int dtype, int tile, hipStream_t s) {
+  if (tile == kTileHalo128x16x32) {
+    if (!conv_halo_supported(a, dtype, tile)) return hipErrorInvalidValue;
+    return conv_halo_go<128, 16, 32, 2, 4>(a, s);
+  }
   if (dtype == kBF16) {
     if (tile == kTileDma256x128) return conv_dma_go<256, 128, 2, 2, 3, 2>(a, s);
-    if (tile == kTileDma256x256) return conv_dma_go<256, 256, 2, 2, 4, 1>(a, s);
+    if (tile == kTileDma256x256) return conv_dma_go<256, 256, 2, 2, 4, 1, true>(a, s);
     if (tile == kTileDma128x256) return conv_dma_go<128, 256, 2, 2, 3, 2>(a, s);
     if (tile == kTileDma128x128) return conv_dma_go<128, 128, 2, 2, 4, 2>(a, s);
     if (tile == kTileDma16x256) return conv_dma_go<16, 256, 1, 4, 4, 2>(a, s);

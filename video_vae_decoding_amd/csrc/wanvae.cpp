@@ -15,6 +15,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -328,19 +329,27 @@ static int prep_vec(Arena& ar, int dtype, const wanvae_tensor* g, int C, float*&
 
 // Tile of the conv kernel for a layer. WANVAE_CONV_TILE (a ConvTile value) overrides the
 // choice for the bf16 layers with more than 64 output channels, for tuning.
-static int pick_tile(int Cout, int64_t M, int mode, int dtype) {
-  static const int forced = [] {
-    const char* e = getenv("WANVAE_CONV_TILE");
-    return e ? atoi(e) : -1;
-  }();
+static std::atomic<int> g_conv_kernel{[] {
+  const char* e = getenv("WANVAE_CONV_TILE");
+  const int k = e ? atoi(e) : -1;
+  return k >= -1 && k < WANVAE_CONV_KERNELS ? k : -1;
+}()};
+
+static int pick_tile(const ConvArgs& a, int dtype) {
+  const int forced = g_conv_kernel.load(std::memory_order_relaxed);
+  const int Cout = a.Cout;
+  const int64_t M = (int64_t)a.F * a.B * a.Ho * a.Wo;
   // bf16: the direct-to-LDS kernels (Cout % 8 == 0 for the frame / interleave / q-k-v stores;
   // the unpatchify + clamp store of conv_out on the 16-channel tile)
-  if (dtype == kBF16 && mode == kEpiVideo && Cout <= 16 && Cout % 4 == 0) return kTileDma16x256;
-  const bool dma_ok = dtype == kBF16 && mode != kEpiVideo && Cout % 8 == 0 && Cout > 64;
+  if (dtype == kBF16 && a.mode == kEpiVideo && Cout <= 16 && Cout % 4 == 0) return kTileDma16x256;
+  const bool dma_ok = dtype == kBF16 && a.mode != kEpiVideo && Cout % 8 == 0 && Cout > 64;
   if (!dma_ok) return Cout <= 64 ? kTile32x256 : kTile128x128;
-  if (forced >= 0) return forced;
-  // 256 x 256 tiles (8 waves of 64 x 128) where there are enough positions to fill the chip;
-  // 128 x 128 on the level-0 layers (3,520 positions per frame)
+  const bool halo = conv_halo_supported(a, dtype, kTileHalo128x16x32);
+  if (forced >= 0 && (forced != kTileHalo128x16x32 || halo)) return forced;
+  // 3x3 convs on frames of at least 32 x 64: the halo tile (input patch shared by the nine
+  // spatial taps); 256 x 256 tiles (8 waves of 64 x 128) for the other convs with enough
+  // positions to fill the chip; 128 x 128 on the level-0 layers (3,520 positions per frame)
+  if (halo && a.Ho >= 32 && a.Wo >= 64 && M >= 16384) return kTileHalo128x16x32;
   if (M < 16384) return kTileDma128x128;
   return Cout % 256 == 0 ? kTileDma256x256w8b : kTileDma256x128;
 }
@@ -366,7 +375,7 @@ static int run_conv(const ConvW& cw, const FrameRef& in, int B, int Hin, int Win
   a.F = F;
   a.w = cw.w;
   a.bias = cw.b;
-  const int tile = pick_tile(cw.Cout, (int64_t)F * B * Ho * Wo, a.mode, dtype);
+  const int tile = pick_tile(a, dtype);
   // algorithmic FLOPs: every output, every spatial tap, the time taps on real frames
   double taps_real = 0;
   for (int t = 0; t < F; ++t)
@@ -741,6 +750,13 @@ int wanvae_profile_read(int kind, double* ms, int64_t* launches, double* flops, 
   if (launches) *launches = n;
   if (flops) *flops = f;
   if (bytes) *bytes = by;
+  return WANVAE_OK;
+}
+
+int wanvae_set_conv_kernel(int kernel) {
+  if (kernel < -1 || kernel >= WANVAE_CONV_KERNELS)
+    return fail(WANVAE_EARG, "conv kernel %d is not in -1..%d", kernel, WANVAE_CONV_KERNELS - 1);
+  g_conv_kernel.store(kernel);
   return WANVAE_OK;
 }
 

@@ -62,9 +62,10 @@ def lib() -> ctypes.CDLL:
         L.wanvae_last_error.restype = ctypes.c_char_p
         L.wanvae_last_error.argtypes = []
         L.wanvae_version.argtypes = []
+        L.wanvae_set_conv_kernel.argtypes = [ctypes.c_int]
         for f in ("wanvae_decode_workspace_size", "wanvae_decode", "wanvae_causal_conv3d_workspace_size",
                   "wanvae_causal_conv3d", "wanvae_attn_block_workspace_size", "wanvae_attn_block", "wanvae_version",
-                  "wanvae_profile_enable", "wanvae_profile_read"):
+                  "wanvae_profile_enable", "wanvae_profile_read", "wanvae_set_conv_kernel"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -207,6 +208,14 @@ def wanvae_attn_block(x: torch.Tensor, gamma, qkv_w, qkv_b, proj_w, proj_b, layo
 
 
 attn_block = wanvae_attn_block
+
+
+CONV_KERNELS = 11
+
+
+def wanvae_set_conv_kernel(kernel: int) -> None:
+    """Use conv kernel ``kernel`` wherever it can run a conv (-1: each conv's default)."""
+    check(lib().wanvae_set_conv_kernel(kernel))
 
 
 def wanvae_profile_enable(on: bool = True) -> None:
