@@ -813,10 +813,11 @@ __global__ void __launch_bounds__(64 * WGC * WGP, MINB) k_conv_dma(const ConvArg
 // reads the nearest x2 upsampling of its input: the patch is the low-resolution region and
 // two neighbouring output positions read the same pixel.
 //
-// Patch pixels are 64-byte rows of 4 chunks stored at slot chunk ^ ((column >> 2) & 3): 16
-// positions along a row hit distinct banks for any shift, and a shift by whole patch rows
-// keeps the permutation, so every fragment address is a per-lane base (one per column shift
-// and 16-column group) plus a compile-time offset.
+// Patch pixels are 64-byte rows of 4 chunks stored at slot chunk ^ ((column >> 1) & 3). A
+// 16-byte LDS read is served 8 lanes at a time over 128 bytes of banks: with an even patch
+// width, 8 consecutive columns fill those banks exactly, for any column shift, and a shift
+// by whole patch rows keeps the permutation, so every fragment address is a per-lane base
+// (one per column shift and 16-column group) plus a compile-time offset.
 
 // a wave-uniform pointer held in scalar registers (buffer descriptors must be scalar)
 __device__ __forceinline__ const char* scalar_ptr(const void* p) {
@@ -843,6 +844,7 @@ __global__ void __launch_bounds__(64 * WGC * WGP, 1) k_conv_halo(const ConvArgs 
   static_assert(WP % TPX == 0 && TPX % 16 == 0, "each wave holds whole tile rows");
   static_assert(!UP || (RW % 2 == 0 && TPY % 2 == 0), "upsampled rows pair up");
   constexpr int PH = UP ? TPY / 2 + 2 : TPY + 2, PW = UP ? TPX / 2 + 2 : TPX + 2;
+  static_assert(PW % 2 == 0, "the bank permutation needs an even patch width");
   constexpr int P = PH * PW;
   constexpr int NPI = (P + 15) / 16;                  // patch DMA instructions (16 pixels each)
   constexpr int NPW = (NPI + NWAVE - 1) / NWAVE;      // per wave (the spare ones load zeros)
@@ -902,16 +904,16 @@ __global__ void __launch_bounds__(64 * WGC * WGP, 1) k_conv_halo(const ConvArgs 
   for (int i = 0; i < NIW; ++i) woffl[i] = (uint32_t)((((wave * NIW + i) * 16 + lrow) * Ktot + lchunk * 8) * 2);
 
   // patch DMA: instruction i of this wave fills pixels (i * NWAVE + wave) * 16 + lane / 4
+  // (recomputed at each patch issue, once per nine steps, rather than held in registers)
   const int oy = UP ? (Y0 >> 1) - 1 : Y0 - 1, ox = UP ? (X0 >> 1) - 1 : X0 - 1;
-  uint32_t poff[NPW];
-#pragma unroll
-  for (int i = 0; i < NPW; ++i) {
+  const int Hin = a.Hin, Win = a.Win;
+  auto poff = [&](int i) -> uint32_t {
     const int q = (i * NWAVE + wave) * 16 + lrow;
     const int prow = q / PW, pcol = q - prow * PW;
     const int iy = oy + prow, ix = ox + pcol;
-    const bool ok = q < P && iy >= 0 && iy < a.Hin && ix >= 0 && ix < a.Win;
-    poff[i] = ok ? (uint32_t)(((iy * a.Win + ix) * Cin + (lslot ^ ((pcol >> 2) & 3)) * 8) * 2) : kOut;
-  }
+    const bool ok = q < P && iy >= 0 && iy < Hin && ix >= 0 && ix < Win;
+    return ok ? (uint32_t)(((iy * Win + ix) * Cin + (lslot ^ ((pcol >> 1) & 3)) * 8) * 2) : kOut;
+  };
   const uint32_t fbytes = (uint32_t)a.Hin * a.Win * Cin * 2;
   const char* fb0 = nullptr;
   const char* fb1 = nullptr;
@@ -924,11 +926,13 @@ __global__ void __launch_bounds__(64 * WGC * WGP, 1) k_conv_halo(const ConvArgs 
 
   // wofs: byte offset of a group's first tap in a weight row; a patch is (frame base, channel
   // byte offset). Groups advance without divisions: channel block minor, time tap major.
-  auto issue_w = [&](char* buf, int wofs, int j) {
+  // a step past the last loads zeros (an empty descriptor): every wave issues the same loads
+  // at every step, so the wait counts below are constants
+  auto issue_w = [&](char* buf, int wofs, int j, bool valid) {
     const int so = wofs + j * Cin * 2;
+    const uint32_t nb = valid ? wbytes : 0u;
 #pragma unroll
-    for (int i = 0; i < NIW; ++i)
-      buffer_lds16(wbase, wbytes, buf + (wave * NIW + i) * 1024, woffl[i], so);
+    for (int i = 0; i < NIW; ++i) buffer_lds16(wbase, nb, buf + (wave * NIW + i) * 1024, woffl[i], so);
   };
   // a null base (a missing history frame, or past the last group) loads zeros, so that every
   // wave keeps the same count of loads in flight
@@ -936,20 +940,24 @@ __global__ void __launch_bounds__(64 * WGC * WGP, 1) k_conv_halo(const ConvArgs 
     const char* pbase = scalar_ptr(base != nullptr ? base + cb2 : zero);
     const uint32_t pbytes = base != nullptr ? fbytes : 0u;
 #pragma unroll
-    for (int i = 0; i < NPW; ++i) buffer_lds16(pbase, pbytes, buf + (i * NWAVE + wave) * 1024, poff[i], 0);
+    for (int i = 0; i < NPW; ++i) buffer_lds16(pbase, pbytes, buf + (i * NWAVE + wave) * 1024, poff(i), 0);
   };
-  // cursor: (time tap, channel block) of the group after the current one, and its frame
-  int ndt = 0, ncb = 0;
-  const char* nfb = fb0;
-  auto advance = [&]() {
-    ncb += 32;
-    if (ncb == Cin) {
-      ncb = 0;
-      ++ndt;
-      nfb = ndt == 1 ? fb1 : (ndt == 2 ? fb2 : nullptr);  // past the last time tap: zeros
+  // cursors over the step groups (channel block minor, time tap major), advanced without
+  // divisions: (dt1, cb1) names the group after the current one, (dt2, cb2) the one after that
+  int dt1 = 0, cb1 = 0, dt2 = 0, cb2 = 0;
+  const char* fb2p = fb0;
+  auto step_group = [&](int& dt, int& cb) {
+    cb += 32;
+    if (cb == Cin) {
+      cb = 0;
+      ++dt;
     }
   };
-  auto nwofs = [&]() -> int { return (ndt * 9 * Cin + ncb) * 2; };
+  auto frame_of = [&](int dt) -> const char* { return dt == 0 ? fb0 : (dt == 1 ? fb1 : (dt == 2 ? fb2 : nullptr)); };
+  step_group(dt1, cb1);
+  step_group(dt2, cb2);
+  step_group(dt2, cb2);
+  fb2p = frame_of(dt2);
 
   const int wc = wave / WGP, wp = wave % WGP;
   f32x4_t acc[TCN][TPN];
@@ -969,16 +977,64 @@ __global__ void __launch_bounds__(64 * WGC * WGP, 1) k_conv_halo(const ConvArgs 
       const int px = xg * 16 + (lane & 15);
       const int col = UP ? ((px + dx - 1) >> 1) + 1 : px + dx;
       const int wrow = UP ? wp * (RW / 2) : wp * RW;
-      pvb[xg][dx] = (wrow * PW + col) * 64 + (((lane >> 4) ^ ((col >> 2) & 3)) << 4);
+      pvb[xg][dx] = (wrow * PW + col) * 64 + (((lane >> 4) ^ ((col >> 1) & 3)) << 4);
     }
 
+  constexpr int H = TPN / 2;
+  static_assert(TPN % 2 == 0, "two halves of position fragments");
+  uint4 wf[TCN], bf[TPN];
+  auto read_w = [&](const char* wbuf) {
+#pragma unroll
+    for (int ic = 0; ic < TCN; ++ic) wf[ic] = *(const uint4*)(wbuf + wrd + ic * 16 * 64);
+  };
+  // position fragments ip0 .. ip0 + H - 1 of spatial tap j from a patch buffer
+  auto read_b = [&](const char* pbuf, int j, int ip0) {
+    const int dy = j / 3, dx = j % 3;
+#pragma unroll
+    for (int ip = ip0; ip < ip0 + H; ++ip) {
+      const int k = (ip * 16) / TPX, xg = ((ip * 16) % TPX) / 16;
+      const int rowc = UP ? ((k + dy - 1) >> 1) + 1 : k + dy;
+      bf[ip] = *(const uint4*)(pbuf + pvb[xg][dx] + rowc * PW * 64);
+    }
+  };
+  auto mfma_half = [&](int ip0) {
+#pragma unroll
+    for (int ip = ip0; ip < ip0 + H; ++ip)
+#pragma unroll
+      for (int ic = 0; ic < TCN; ++ic) Mma<T>::run(acc[ic][ip], wf[ic], bf[ip]);
+  };
+  // waits until this wave's loads of step x (and, at a group's first step, the group's patch,
+  // issued before them) have landed and its LDS reads have returned, then the barrier. After
+  // W(x) each wave has issued W(x + 1) .. W(x + 7), and the next group's patch when x is not
+  // a group's first step.
+  auto sync_step = [&](int jx) {
+    if (jx == 0)
+      wait_vm_lgkm0<7 * NIW>();
+    else
+      wait_vm_lgkm0<7 * NIW + NPW>();
+    __builtin_amdgcn_s_barrier();
+  };
+
+  // Pipeline. W(x) (the weight tile of step x) goes to buffer x % 9 at the barrier of step
+  // x - 8; the patch of group g + 1 goes to the other patch buffer at the barrier of the
+  // group's first step. The barrier of step s + 1 sits between the two halves of step s's
+  // MFMAs: after it no wave reads step s's weight buffer (its fragments are in registers)
+  // nor the previous group's patch, the first half of step s + 1's position fragments is
+  // read into the registers the first half of step s has finished with, and the second
+  // half of step s's MFMAs covers the read latency.
   char* wb[9] = {w0, w1, w2, w3, w4, w5, w6, w7, w8};
   issue_p(p0, fb0, 0);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) issue_w(wb[j], 0, j);
-  int cur_wofs = 0;
-  advance();  // the cursor names group 1
+  for (int j = 0; j < 8; ++j) issue_w(wb[j], 0, j, true);
+  sync_step(0);
+  issue_w(wb[8], 0, 8, true);
+  issue_p(p1, frame_of(dt1), cb1 * 2);
+  __builtin_amdgcn_sched_barrier(0);
+  read_w(wb[0]);
+  read_b(p0, 0, 0);
+  read_b(p0, 0, H);
 
+  int wofs1 = (dt1 * 9 * Cin + cb1) * 2;  // weight offset of the next group
   for (int g0 = 0; g0 < G; g0 += 2) {
 #pragma unroll
     for (int gg = 0; gg < 2; ++gg) {
@@ -986,43 +1042,31 @@ __global__ void __launch_bounds__(64 * WGC * WGP, 1) k_conv_halo(const ConvArgs 
       if (g < G) {
         char* pcur = gg == 0 ? p0 : p1;
         char* pnext = gg == 0 ? p1 : p0;
-        const int next_wofs = nwofs();
+        // the last step of all reads a finished buffer into registers it leaves unused, so that
+        // every step is the same straight-line code
 #pragma unroll
         for (int j = 0; j < 9; ++j) {
           const int s = 9 * g + j;
-          // this wave's loads of step s (and of the group's patch, issued earlier) have landed
-          if (s + 7 < S) {
-            if (j == 0)
-              wait_vm_lgkm0<7 * NIW>();
-            else
-              wait_vm_lgkm0<7 * NIW + NPW>();
-          } else {
-            wait_vm_lgkm0<0>();
-          }
-          __builtin_amdgcn_s_barrier();
-          // refill the buffer of step s - 1 with step s + 8; at a group's first step, the
-          // patch of the next group goes to the buffer the previous group used
-          if (s + 8 < S) issue_w(wb[(j + 8) % 9], j == 0 ? cur_wofs : next_wofs, (j + 8) % 9);
-          if (j == 0) issue_p(pnext, nfb, ncb * 2);
+          const int jn = (j + 1) % 9;
+          char* pn = j == 8 ? pnext : pcur;  // patch of step s + 1
+          mfma_half(0);
           __builtin_amdgcn_sched_barrier(0);
-          const int dy = j / 3, dx = j % 3;
-          uint4 wf[TCN], bf[TPN];
-#pragma unroll
-          for (int ic = 0; ic < TCN; ++ic) wf[ic] = *(const uint4*)(wb[j] + wrd + ic * 16 * 64);
-#pragma unroll
-          for (int ip = 0; ip < TPN; ++ip) {
-            const int k = (ip * 16) / TPX, xg = ((ip * 16) % TPX) / 16;
-            const int rowc = UP ? ((k + dy - 1) >> 1) + 1 : k + dy;
-            bf[ip] = *(const uint4*)(pcur + pvb[xg][dx] + rowc * PW * 64);
-          }
+          sync_step(jn);
+          issue_w(wb[j], wofs1, j, s + 9 < S);
+          if (j == 8) issue_p(pcur, fb2p, cb2 * 2);
           __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int ip = 0; ip < TPN; ++ip)
-#pragma unroll
-            for (int ic = 0; ic < TCN; ++ic) Mma<T>::run(acc[ic][ip], wf[ic], bf[ip]);
+          read_b(pn, jn, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          mfma_half(H);
+          __builtin_amdgcn_sched_barrier(0);
+          read_w(wb[jn]);
+          read_b(pn, jn, H);
         }
-        cur_wofs = next_wofs;
-        advance();
+        // the cursors move one group on
+        step_group(dt1, cb1);
+        wofs1 = (dt1 * 9 * Cin + cb1) * 2;
+        step_group(dt2, cb2);
+        fb2p = frame_of(dt2);
       }
     }
   }
