@@ -6,13 +6,17 @@ One step = one whole decode, wanvae_decode through the C ABI, of seeded syntheti
 accumulation) -> video [1, 3, 121, 704, 1280]. The latents and the fp32 weights are resident
 in HBM before the timed region; the decode's own weight rounding/repacking is inside it.
 
-Prints one JSON line: decoded frames/s, the dominant kernel's roofline (the implicit-GEMM
-conv: algorithmic FLOPs / HIP-event kernel time over the timed region, against the bf16
-dense MFMA peak), the other kernel classes, and the CPU oracle timed on a bounded sample.
+Prints one JSON line: decoded frames/s, the dominant kernel's roofline (the conv kernels,
+all launches of the timed decodes: algorithmic FLOPs / HIP-event kernel time, against the
+bf16 dense MFMA peak; the HBM bytes per launch from the stored counter measurement while the
+kernel source it was taken on is unchanged), the other kernel classes, and the CPU oracle
+timed on a bounded sample.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+    python bench.py --copy-bytes N    # three device-to-device copies of N bytes (counter scale)
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -27,6 +31,8 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 FL
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 METRIC = "decoded frames/s (TI2V-5B VAE, 704x1280 bf16); conv TFLOP/s % MFMA peak"
+TRAFFIC = os.path.join(ROOT, "profiles", "conv_traffic_704x1280_bf16.json")
+KERNELS_SRC = os.path.join(ROOT, "video_vae_decoding_amd", "csrc", "kernels.hip")
 
 
 def log(*a):
@@ -52,17 +58,46 @@ def cpu_baseline(cfg, W):
                       "value = (1/16 frame) / seconds"}
 
 
+def stored_traffic():
+    """HBM bytes per conv launch (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's reading),
+    from the stored counter measurement; None once the kernel source differs from the one
+    the counters were taken on."""
+    if not os.path.exists(TRAFFIC):
+        return None
+    with open(TRAFFIC) as f:
+        t = json.load(f)
+    with open(KERNELS_SRC, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != t["kernels_hip_sha256"]:
+            return None
+    return t["hbm_bytes_per_launch"]
+
+
+def copy_calibration(nbytes):
+    import torch
+    x = torch.ones(nbytes, dtype=torch.uint8, device="cuda:0")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "copies": 3}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the decoder here runs on a single MI355X (got --gpus {args.gpus}); "
               "run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.copy_bytes:
+        copy_calibration(args.copy_bytes)
+        return
 
     import torch
 
@@ -124,9 +159,10 @@ def main():
         "config": {"workload": "ti2v5b_vae_decode_704x1280x121_bf16", "latent": [cfg.B, 48, cfg.T, cfg.h, cfg.w],
                    "video": [cfg.B, 3, cfg.frames, 16 * cfg.h, 16 * cfg.w], "weights": "random-init, seed 3",
                    "accumulate": "fp32"},
-        "roofline": {"bound": "mfma", "kernel": "k_conv<bf16> (implicit-GEMM causal conv, all launches of a decode)",
+        "roofline": {"bound": "mfma",
+                     "kernel": "conv (k_conv_halo for the 3x3 convs, k_conv_dma for the rest; all launches of a decode)",
                      "achieved": round(conv_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(conv_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(conv_tflops / PEAK_BF16_TFLOPS, 4), "traffic": stored_traffic(),
                      "launches": conv["launches"], "avg_launch_ms": round(conv["ms"] / max(1, conv["launches"]), 4),
                      "algorithmic_tflop_per_step": round(conv["flops"] / args.steps / 1e12, 2)},
         "kernels": kernels,
