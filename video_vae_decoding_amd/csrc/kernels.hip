@@ -980,28 +980,25 @@ __global__ void __launch_bounds__(64 * WGC * WGP, 1) k_conv_halo(const ConvArgs 
       pvb[xg][dx] = (wrow * PW + col) * 64 + (((lane >> 4) ^ ((col >> 1) & 3)) << 4);
     }
 
-  constexpr int H = TPN / 2;
-  static_assert(TPN % 2 == 0, "two halves of position fragments");
-  uint4 wf[TCN], bf[TPN];
-  auto read_w = [&](const char* wbuf) {
-#pragma unroll
-    for (int ic = 0; ic < TCN; ++ic) wf[ic] = *(const uint4*)(wbuf + wrd + ic * 16 * 64);
-  };
-  // position fragments ip0 .. ip0 + H - 1 of spatial tap j from a patch buffer
-  auto read_b = [&](const char* pbuf, int j, int ip0) {
+  // two register sets of fragments: step s computes from set s & 1 while step s + 1's
+  // fragments are read into the other
+  uint4 wf[2][TCN], bf[2][TPN];
+  auto read_frags = [&](int set, const char* wbuf, const char* pbuf, int j) {
     const int dy = j / 3, dx = j % 3;
 #pragma unroll
-    for (int ip = ip0; ip < ip0 + H; ++ip) {
+    for (int ic = 0; ic < TCN; ++ic) wf[set][ic] = *(const uint4*)(wbuf + wrd + ic * 16 * 64);
+#pragma unroll
+    for (int ip = 0; ip < TPN; ++ip) {
       const int k = (ip * 16) / TPX, xg = ((ip * 16) % TPX) / 16;
       const int rowc = UP ? ((k + dy - 1) >> 1) + 1 : k + dy;
-      bf[ip] = *(const uint4*)(pbuf + pvb[xg][dx] + rowc * PW * 64);
+      bf[set][ip] = *(const uint4*)(pbuf + pvb[xg][dx] + rowc * PW * 64);
     }
   };
-  auto mfma_half = [&](int ip0) {
+  auto mfma_all = [&](int set) {
 #pragma unroll
-    for (int ip = ip0; ip < ip0 + H; ++ip)
+    for (int ip = 0; ip < TPN; ++ip)
 #pragma unroll
-      for (int ic = 0; ic < TCN; ++ic) Mma<T>::run(acc[ic][ip], wf[ic], bf[ip]);
+      for (int ic = 0; ic < TCN; ++ic) Mma<T>::run(acc[ic][ip], wf[set][ic], bf[set][ip]);
   };
   // waits until this wave's loads of step x (and, at a group's first step, the group's patch,
   // issued before them) have landed and its LDS reads have returned, then the barrier. After
@@ -1017,11 +1014,10 @@ __global__ void __launch_bounds__(64 * WGC * WGP, 1) k_conv_halo(const ConvArgs 
 
   // Pipeline. W(x) (the weight tile of step x) goes to buffer x % 9 at the barrier of step
   // x - 8; the patch of group g + 1 goes to the other patch buffer at the barrier of the
-  // group's first step. The barrier of step s + 1 sits between the two halves of step s's
-  // MFMAs: after it no wave reads step s's weight buffer (its fragments are in registers)
-  // nor the previous group's patch, the first half of step s + 1's position fragments is
-  // read into the registers the first half of step s has finished with, and the second
-  // half of step s's MFMAs covers the read latency.
+  // group's first step. Step s begins with the barrier of step s + 1: step s's fragments are
+  // already in registers, so no wave reads step s's weight buffer nor the previous group's
+  // patch any more, and step s + 1's fragments are read into the other register set between
+  // step s's MFMAs.
   char* wb[9] = {w0, w1, w2, w3, w4, w5, w6, w7, w8};
   issue_p(p0, fb0, 0);
 #pragma unroll
@@ -1030,9 +1026,7 @@ __global__ void __launch_bounds__(64 * WGC * WGP, 1) k_conv_halo(const ConvArgs 
   issue_w(wb[8], 0, 8, true);
   issue_p(p1, frame_of(dt1), cb1 * 2);
   __builtin_amdgcn_sched_barrier(0);
-  read_w(wb[0]);
-  read_b(p0, 0, 0);
-  read_b(p0, 0, H);
+  read_frags(0, wb[0], p0, 0);
 
   int wofs1 = (dt1 * 9 * Cin + cb1) * 2;  // weight offset of the next group
   for (int g0 = 0; g0 < G; g0 += 2) {
@@ -1042,25 +1036,26 @@ __global__ void __launch_bounds__(64 * WGC * WGP, 1) k_conv_halo(const ConvArgs 
       if (g < G) {
         char* pcur = gg == 0 ? p0 : p1;
         char* pnext = gg == 0 ? p1 : p0;
-        // the last step of all reads a finished buffer into registers it leaves unused, so that
+        // the last step of all reads a finished buffer into the set it leaves unused, so that
         // every step is the same straight-line code
 #pragma unroll
         for (int j = 0; j < 9; ++j) {
           const int s = 9 * g + j;
+          const int set = (9 * gg + j) & 1;
           const int jn = (j + 1) % 9;
-          char* pn = j == 8 ? pnext : pcur;  // patch of step s + 1
-          mfma_half(0);
-          __builtin_amdgcn_sched_barrier(0);
           sync_step(jn);
           issue_w(wb[j], wofs1, j, s + 9 < S);
           if (j == 8) issue_p(pcur, fb2p, cb2 * 2);
           __builtin_amdgcn_sched_barrier(0);
-          read_b(pn, jn, 0);
+          read_frags(set ^ 1, wb[jn], j == 8 ? pnext : pcur, jn);
+          mfma_all(set);
+          // one LDS read between groups of MFMAs
+#pragma unroll
+          for (int r = 0; r < TCN + TPN; ++r) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, (TCN * TPN) / (TCN + TPN), 0);
+          }
           __builtin_amdgcn_sched_barrier(0);
-          mfma_half(H);
-          __builtin_amdgcn_sched_barrier(0);
-          read_w(wb[jn]);
-          read_b(pn, jn, H);
         }
         // the cursors move one group on
         step_group(dt1, cb1);
