@@ -51,6 +51,8 @@ struct ConvArgs {
   void* k;
   void* vt;
   int S, Sp;
+  int ksplit;             // >= 1: K ranges of the direct-to-LDS kernels (> 1: bf16, Cout % 8 == 0,
+  float* part;            //   not the video epilogue); float32 partials [ksplit][M][Cout]
 };
 
 struct NormArgs {

@@ -466,12 +466,18 @@ __global__ void __launch_bounds__(64 * WGC * WGP, MINB) k_conv_dma(const ConvArg
   const int HWo = a.Ho * a.Wo;
   const int M = a.F * a.B * HWo;
   const int nct = (a.Cout + TC - 1) / TC;
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int ntiles = nct * ((M + TP - 1) / TP);
+  // split K: workgroup z of a.ksplit takes the z-th contiguous range of K steps; the tiles of
+  // one range are adjacent (they share its weight rows)
+  const int bid0 = xcd_remap(blockIdx.x, gridDim.x);
+  const int kz = __builtin_amdgcn_readfirstlane(bid0 / ntiles), bid = bid0 - kz * ntiles;
   const int ct = bid % nct, pt = bid / nct;
   const int c0 = ct * TC, m0 = pt * TP;
   const int khw = a.kh * a.kw, taps = a.kt * khw;
   const int csteps = (a.Cin + 31) / 32;
-  const int steps = taps * csteps;
+  const int all_steps = taps * csteps;
+  const int s_begin = (int)((int64_t)all_steps * kz / a.ksplit);
+  const int steps = (int)((int64_t)all_steps * (kz + 1) / a.ksplit) - s_begin;
   const int64_t Ktot = (int64_t)taps * a.Cin;
   const int ph = a.kh >> 1, pw = a.kw >> 1;
   const char* zero = (const char*)g_zero_page;
@@ -527,8 +533,13 @@ __global__ void __launch_bounds__(64 * WGC * WGP, MINB) k_conv_dma(const ConvArg
   // without divisions; per tap each A row's source pointer (the zero page where the tap reads
   // zeros: padding, a missing history frame, a position past the end)
   const char* ap[NIA];
-  int cdt = 0, cdy = 0, cdx = 0, ccs = 0;
-  int64_t woff = 0;
+  // the cursor starts at step s_begin: tap s_begin / csteps, channel block s_begin % csteps
+  const int tap0 = s_begin / csteps;
+  int ccs = s_begin - tap0 * csteps;
+  int cdt = tap0 / khw;
+  int cdy = (tap0 - cdt * khw) / a.kw;
+  int cdx = tap0 - cdt * khw - cdy * a.kw;
+  int64_t woff = (int64_t)tap0 * a.Cin;
   auto set_tap = [&]() {
 #pragma unroll
     for (int i = 0; i < NIA; ++i) {
@@ -717,6 +728,22 @@ __global__ void __launch_bounds__(64 * WGC * WGP, MINB) k_conv_dma(const ConvArg
     }
   }
 
+  if (a.ksplit > 1) {
+    // split K: the raw float32 sums of this K range go to the partials buffer
+    // [ksplit][M][Cout]; k_splitk_reduce adds the ranges in order and runs the epilogue
+#pragma unroll
+    for (int ip = 0; ip < TPN; ++ip) {
+      const int m = m0 + wp * WP + ip * 16 + (lane & 15);
+#pragma unroll
+      for (int ic = 0; ic < TCN; ++ic) {
+        const int c = c0 + wc * WC + ic * 16 + 4 * (lane >> 4);
+        if (m < M && c < a.Cout)
+          *(float4*)(a.part + ((int64_t)kz * M + m) * a.Cout + c) =
+              make_float4(acc[ic][ip][0], acc[ic][ip][1], acc[ic][ip][2], acc[ic][ip][3]);
+      }
+    }
+    return;
+  }
   // Epilogue through LDS. Each lane rounds acc + bias to bf16 and writes its 4 channels of
   // one position into the C tile held in the (now idle) stage buffers: rows are positions of
   // TC channels, 8-byte slots permuted by slot ^ (row & 15) so the 16 positions of a fragment
@@ -800,6 +827,35 @@ __global__ void __launch_bounds__(64 * WGC * WGP, MINB) k_conv_dma(const ConvArg
       }
     }
   }
+}
+
+// Split-K finish: out = epilogue(R(sum over the K ranges, in order, + bias)), one thread per
+// 8 channels of one position. The same rounding points as the one-pass epilogue.
+__global__ void __launch_bounds__(256) k_splitk_reduce(const ConvArgs a) {
+  const int UPR = a.Cout / 8;
+  const int64_t M = (int64_t)a.F * a.B * a.Ho * a.Wo;
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (u >= M * UPR) return;
+  const int64_t m = u / UPR;
+  const int c = (int)(u - m * UPR) * 8;
+  float v[8];
+  const float4 b0 = *(const float4*)(a.bias + c), b1 = *(const float4*)(a.bias + c + 4);
+  float s8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int z = 0; z < a.ksplit; ++z) {
+    const float* p = a.part + ((int64_t)z * M + m) * a.Cout + c;
+    const float4 x0 = *(const float4*)p, x1 = *(const float4*)(p + 4);
+    s8[0] += x0.x, s8[1] += x0.y, s8[2] += x0.z, s8[3] += x0.w;
+    s8[4] += x1.x, s8[5] += x1.y, s8[6] += x1.z, s8[7] += x1.w;
+  }
+  const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = bf2f(f2bf(s8[e] + bb[e]));
+  const int x = (int)(m % a.Wo);
+  int64_t q = m / a.Wo;
+  const int y = (int)(q % a.Ho);
+  q /= a.Ho;
+  const int b = (int)(q % a.B), t = (int)(q / a.B);
+  epilogue8_bf16(a, t, b, y, x, c, v);
 }
 
 // ------------------------------------------------------------------ 3x3 conv with a halo tile (bf16)
@@ -1489,9 +1545,9 @@ static hipError_t conv_go(const ConvArgs& a, hipStream_t s) {
 }
 
 template <int TC, int TP, int WGC, int WGP, int STAGES, int MINB, bool RB2 = false>
-static hipError_t conv_dma_go(const ConvArgs& a, hipStream_t s) {
+static hipError_t conv_dma_launch(const ConvArgs& a, hipStream_t s) {
   const int64_t M = (int64_t)a.F * a.B * a.Ho * a.Wo;
-  const int64_t blocks = ((a.Cout + TC - 1) / TC) * ((M + TP - 1) / TP);
+  const int64_t blocks = ((a.Cout + TC - 1) / TC) * ((M + TP - 1) / TP) * a.ksplit;
   // the aligned path loads every wave's weight rows unconditionally: only where they all lie
   // in the tile (16 rows per wave and instruction), not on the 16-channel tile
   if constexpr (TC >= 16 * WGC * WGP) {
@@ -1504,6 +1560,17 @@ static hipError_t conv_dma_go(const ConvArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((k_conv_dma<TC, TP, WGC, WGP, STAGES, MINB, false, RB2>), dim3((unsigned)blocks),
                      dim3(64 * WGC * WGP), 0, s, a);
   return hipGetLastError();
+}
+
+template <int TC, int TP, int WGC, int WGP, int STAGES, int MINB, bool RB2 = false>
+static hipError_t conv_dma_go(const ConvArgs& a, hipStream_t s) {
+  if (hipError_t e = conv_dma_launch<TC, TP, WGC, WGP, STAGES, MINB, RB2>(a, s)) return e;
+  if (a.ksplit > 1) {
+    const int64_t units = (int64_t)a.F * a.B * a.Ho * a.Wo * (a.Cout / 8);
+    hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 template <int TC, int TPY, int TPX, int WGC, int WGP>

@@ -354,6 +354,53 @@ static int pick_tile(const ConvArgs& a, int dtype) {
   return Cout % 256 == 0 ? kTileDma256x256w8b : kTileDma256x128;
 }
 
+// Scratch for the float32 partial sums of split-K convs, set by the entry point for the
+// duration of a call (thread-local: calls are synchronous on their host thread).
+struct SplitBuf {
+  float* p = nullptr;
+  size_t floats = 0;
+};
+static thread_local SplitBuf t_split;
+struct SplitScope {
+  SplitBuf prev;
+  explicit SplitScope(SplitBuf b) : prev(t_split) { t_split = b; }
+  ~SplitScope() { t_split = prev; }
+};
+
+// Partial-sum floats to reserve for convs over M positions with up to Cout channels: convs
+// with fewer than 16,384 positions (the 128 x 128 tile) split K up to 4 ways.
+static size_t split_floats(int64_t M, int64_t Cout) { return M < 16384 ? (size_t)4 * M * Cout : 0; }
+
+static SplitBuf take_split(Arena& ar, int64_t M, int64_t Cout) {
+  SplitBuf b;
+  b.floats = split_floats(M, Cout);
+  if (b.floats) b.p = (float*)ar.take(b.floats * 4);
+  return b;
+}
+
+// K split of a direct-to-LDS conv: enough workgroups for about three per CU when the tiles
+// alone leave the chip short, at least 16 K steps per range, within the partials scratch.
+static int split_for(const ConvArgs& a, int tile, int dtype, const SplitBuf& sb) {
+  int TC = 0, TP = 0;
+  switch (tile) {
+    case kTileDma256x128: TC = 256, TP = 128; break;
+    case kTileDma256x256: case kTileDma256x256w8: case kTileDma256x256w8b: TC = 256, TP = 256; break;
+    case kTileDma128x128: TC = 128, TP = 128; break;
+    case kTileDma128x256: TC = 128, TP = 256; break;
+    case kTileDma16x256: TC = 16, TP = 256; break;
+    default: return 1;
+  }
+  if (dtype != kBF16 || a.mode == kEpiVideo || a.Cout % 8 || sb.p == nullptr) return 1;
+  const int64_t M = (int64_t)a.F * a.B * a.Ho * a.Wo;
+  const int64_t tiles = ((a.Cout + TC - 1) / TC) * ((M + TP - 1) / TP);
+  const int steps = a.kt * a.kh * a.kw * ((a.Cin + 31) / 32);
+  if (tiles >= 512) return 1;
+  int ks = (int)std::min<int64_t>(4, (768 + tiles - 1) / tiles);
+  ks = std::min(ks, steps / 16);
+  while (ks > 1 && (size_t)ks * M * a.Cout > sb.floats) --ks;
+  return std::max(ks, 1);
+}
+
 struct ConvCall {
   ConvArgs a;
   ConvCall() { memset(&a, 0, sizeof a); }
@@ -376,6 +423,8 @@ static int run_conv(const ConvW& cw, const FrameRef& in, int B, int Hin, int Win
   a.w = cw.w;
   a.bias = cw.b;
   const int tile = pick_tile(a, dtype);
+  a.ksplit = split_for(a, tile, dtype, t_split);
+  a.part = t_split.p;
   // algorithmic FLOPs: every output, every spatial tap, the time taps on real frames
   double taps_real = 0;
   for (int t = 0; t < F; ++t)
@@ -429,9 +478,10 @@ static int run_norm(const FrameRef& in, const FrameRef& out, int F, int B, int H
 struct AttnBufs {
   void *n = nullptr, *q = nullptr, *k = nullptr, *vt = nullptr, *o = nullptr;
   int S = 0, Sp = 0;
+  SplitBuf split;  // the standalone block's split-K scratch (the decoder has its own)
 };
 
-static void plan_attn_bufs(Arena& ar, AttnBufs& ab, int nfr, int S, int C, int dtype) {
+static void plan_attn_bufs(Arena& ar, AttnBufs& ab, int nfr, int S, int C, int dtype, bool with_split) {
   const size_t es = esize(dtype);
   ab.S = S;
   ab.Sp = (int)align_up(S, 32);
@@ -440,6 +490,7 @@ static void plan_attn_bufs(Arena& ar, AttnBufs& ab, int nfr, int S, int C, int d
   ab.k = ar.take((size_t)nfr * S * C * es);
   ab.vt = ar.take((size_t)nfr * C * ab.Sp * es);
   ab.o = ar.take((size_t)nfr * S * C * es);
+  if (with_split) ab.split = take_split(ar, (int64_t)nfr * S, 3 * (int64_t)C);
 }
 
 static int run_attn(const FrameRef& x, const FrameRef& y, int nfr, int H, int W, int C, const float* gamma,
@@ -539,11 +590,15 @@ class Decoder {
       if (u[i].temporal) ring(p + ".upsampler.time_conv", i, u[i].cout);
     }
     ring("decoder.conv_out", 3, c1);
-    plan_attn_bufs(ar, ab_, B_, h_ * w_, c4, dt_);
+    plan_attn_bufs(ar, ab_, B_, h_ * w_, c4, dt_, false);
+    // split-K scratch for the level-0 convs (one frame of B x h x w positions; at most 3 c4
+    // output channels, the attention's q-k-v conv)
+    split_ = take_split(ar, (int64_t)B_ * h_ * w_, 3 * (int64_t)c4);
     return WANVAE_OK;
   }
 
   int run(const void* z, int z_dtype, void* video) {
+    SplitScope scope(split_);
     const int64_t zf = (int64_t)B_ * h_ * w_ * tp_.z;
     HIP_TRY(launch_ncthw_to_frames(z, z_dtype, zt_, dt_, B_, tp_.z, tp_.z, T_, h_, w_, st_));
     {  // post_quant_conv over all T latent frames at once (frames folded into the batch)
@@ -697,6 +752,7 @@ class Decoder {
   void* zt_ = nullptr;
   void* pq_ = nullptr;
   AttnBufs ab_;
+  SplitBuf split_;
 };
 
 static int check_dtype(int dtype, const char* what) {
@@ -842,6 +898,7 @@ static size_t conv_ws(int64_t B, int64_t Cin, int64_t Cout, int64_t taps, int64_
     ar.take((size_t)(t + n_cache) * B * h * w * Cin * esize(dtype));
     ar.take((size_t)t * B * h * w * Cout * esize(dtype));
   }
+  take_split(ar, t * B * h * w, Cout);
   return ar.used;
 }
 
@@ -898,6 +955,7 @@ int wanvae_causal_conv3d(const void* x, const void* cache, int64_t B, int64_t Ci
     out = frames_of(y, (int)t, hw * Cout, t * hw * Cout, es);
   }
   if (rc == WANVAE_OK) {
+    SplitScope scope(take_split(ar, t * B * h * w, Cout));
     ConvCall cc;
     cc.a.mode = kEpiFrames;
     set_out(cc.a, out, Cout);
@@ -950,7 +1008,7 @@ static size_t attn_ws(int64_t B, int64_t C, int64_t T, int64_t h, int64_t w, int
   ar.take((size_t)C * 4);
   ar.take((size_t)C * 4);
   AttnBufs ab;
-  plan_attn_bufs(ar, ab, (int)(B * T), (int)(h * w), (int)C, dtype);
+  plan_attn_bufs(ar, ab, (int)(B * T), (int)(h * w), (int)C, dtype, true);
   if (layout == WANVAE_NCTHW) {
     ar.take((size_t)B * T * h * w * C * es);
     ar.take((size_t)B * T * h * w * C * es);
@@ -990,7 +1048,8 @@ int wanvae_attn_block(const void* x, int32_t layout, int64_t B, int64_t C, int64
   if (rc == WANVAE_OK) rc = prep_conv(ar, dtype, proj_w, proj_b, Ci, Ci, 1, 1, 1, proj, st);
   if (rc == WANVAE_OK) rc = prep_vec(ar, dtype, gamma, Ci, g, st);
   AttnBufs ab;
-  plan_attn_bufs(ar, ab, nfr, S, Ci, dtype);
+  plan_attn_bufs(ar, ab, nfr, S, Ci, dtype, true);
+  SplitScope scope(ab.split);
   // frames folded into the batch: frame index b' = t * B + b (NCTHW, converted) or b * T + t (NTHWC)
   const void* xf = x;
   void* yf = y;
