@@ -907,9 +907,14 @@ __global__ void __launch_bounds__(64 * WGC * WGP, 1) k_conv_halo(const ConvArgs 
   constexpr int RB = TC * 2;                          // epilogue staging row (bf16 channels)
   // a patch buffer also holds a quarter of the C tile for the epilogue
   constexpr int PBUF = NPW * NWAVE * 1024 > TP / 4 * RB ? NPW * NWAVE * 1024 : TP / 4 * RB;
-  constexpr int NIW = TC / (16 * NWAVE);              // weight DMA instructions per wave per step
-  static_assert(NIW >= 1 && NIW * 16 * NWAVE == TC, "weight rows per wave");
-  constexpr int WBUF = TC * 64;
+  // weight DMA instructions per wave per step (16 rows each). A tile of fewer than 16 rows
+  // per wave (the 16-channel tile of conv_out) has one instruction per wave too: the waves
+  // past the tile load zeros into a spare 1 KB slot, so that every wave keeps the same count
+  // of loads in flight.
+  constexpr bool WSPARE = TC < 16 * NWAVE;
+  constexpr int NIW = WSPARE ? 1 : TC / (16 * NWAVE);
+  static_assert(WSPARE ? TC == 16 : NIW * 16 * NWAVE == TC, "weight rows per wave");
+  constexpr int WBUF = TC * 64 + (WSPARE ? 1024 : 0);
   constexpr int RPA = PBUF / RB;
   static_assert(2 * RPA >= TP / 2, "half the C tile fits the patch buffers");
   __shared__ __attribute__((aligned(1024))) char p0[PBUF];
@@ -926,7 +931,7 @@ __global__ void __launch_bounds__(64 * WGC * WGP, 1) k_conv_halo(const ConvArgs 
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nct = a.Cout / TC;
+  const int nct = (a.Cout + TC - 1) / TC;
   const int tiles_x = (a.Wo + TPX - 1) / TPX, tiles_y = (a.Ho + TPY - 1) / TPY;
   // block coordinates are wave-uniform: keep them scalar so that the frame tables are read
   // with scalar loads
@@ -953,11 +958,14 @@ __global__ void __launch_bounds__(64 * WGC * WGP, 1) k_conv_halo(const ConvArgs 
   constexpr uint32_t kOut = 0x80000000u;  // offset beyond every descriptor: zeros
   // weight DMA: as in k_conv_dma (rows of 64 bytes, slot = chunk ^ ((row >> 1) & 3))
   const int lchunk = lslot ^ ((lrow >> 1) & 3);
+  // rows past Cout lie past the descriptor's size and read as zeros
   const char* wbase = scalar_ptr((const T*)a.w + (int64_t)c0 * Ktot);
-  const uint32_t wbytes = (uint32_t)(TC * Ktot * 2);
+  const uint32_t wbytes = (uint32_t)((a.Cout - c0 < TC ? a.Cout - c0 : TC) * Ktot * 2);
   uint32_t woffl[NIW];
 #pragma unroll
   for (int i = 0; i < NIW; ++i) woffl[i] = (uint32_t)((((wave * NIW + i) * 16 + lrow) * Ktot + lchunk * 8) * 2);
+  // the LDS row of a wave's weight instruction (the spare slot for the waves past the tile)
+  auto wdst = [&](int i) { return WSPARE && wave > 0 ? TC * 64 : (wave * NIW + i) * 1024; };
 
   // patch DMA: instruction i of this wave fills pixels (i * NWAVE + wave) * 16 + lane / 4
   // (recomputed at each patch issue, once per nine steps, rather than held in registers)
@@ -986,9 +994,9 @@ __global__ void __launch_bounds__(64 * WGC * WGP, 1) k_conv_halo(const ConvArgs 
   // at every step, so the wait counts below are constants
   auto issue_w = [&](char* buf, int wofs, int j, bool valid) {
     const int so = wofs + j * Cin * 2;
-    const uint32_t nb = valid ? wbytes : 0u;
+    const uint32_t nb = valid && !(WSPARE && wave > 0) ? wbytes : 0u;
 #pragma unroll
-    for (int i = 0; i < NIW; ++i) buffer_lds16(wbase, nb, buf + (wave * NIW + i) * 1024, woffl[i], so);
+    for (int i = 0; i < NIW; ++i) buffer_lds16(wbase, nb, buf + wdst(i), woffl[i], so);
   };
   // a null base (a missing history frame, or past the last group) loads zeros, so that every
   // wave keeps the same count of loads in flight
@@ -1106,10 +1114,11 @@ __global__ void __launch_bounds__(64 * WGC * WGP, 1) k_conv_halo(const ConvArgs 
           read_frags(set ^ 1, wb[jn], j == 8 ? pnext : pcur, jn);
           mfma_all(set);
           // one LDS read between groups of MFMAs
+          constexpr int MPR = (TCN * TPN + TCN + TPN - 1) / (TCN + TPN);
 #pragma unroll
           for (int r = 0; r < TCN + TPN; ++r) {
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, (TCN * TPN) / (TCN + TPN), 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, MPR, 0);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -1128,9 +1137,12 @@ __global__ void __launch_bounds__(64 * WGC * WGP, 1) k_conv_halo(const ConvArgs 
   wait_vm_lgkm0<0>();
   constexpr int SWZ = TC / 4 - 1 < 15 ? TC / 4 - 1 : 15;
   auto crow = [&](int r) -> char* { return r < RPA ? p0 + r * RB : p1 + (r - RPA) * RB; };
-  float4 bias[TCN];
+  float4 bias[TCN];  // (Cout is a multiple of 4: a lane's 4 channels all exist or all do not)
 #pragma unroll
-  for (int ic = 0; ic < TCN; ++ic) bias[ic] = *(const float4*)(a.bias + c0 + wc * WC + ic * 16 + 4 * (lane >> 4));
+  for (int ic = 0; ic < TCN; ++ic) {
+    const int c = c0 + wc * WC + ic * 16 + 4 * (lane >> 4);
+    bias[ic] = c < a.Cout ? *(const float4*)(a.bias + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   constexpr int UPR = TC / 8;
   static_assert(NT % UPR == 0, "units per row divide the workgroup");
   constexpr int PSTEP = NT / UPR;
@@ -1154,16 +1166,31 @@ __global__ void __launch_bounds__(64 * WGC * WGP, 1) k_conv_halo(const ConvArgs 
       }
     }
     __syncthreads();
-    for (int r = tid / UPR; r < TP / 2; r += PSTEP) {
-      const int p = h * (TP / 2) + r;
-      const int y = Y0 + p / TPX, x = X0 + p % TPX;
-      if (y < a.Ho && x < a.Wo) {
-        const char* row = crow(r);
-        const uint2 lo = *(const uint2*)(row + (((2 * cu) ^ (r & SWZ)) << 3));
-        const uint2 hi = *(const uint2*)(row + (((2 * cu + 1) ^ (r & SWZ)) << 3));
-        float v[8];
-        unpack8_bf16(make_uint4(lo.x, lo.y, hi.x, hi.y), v);
-        epilogue8_bf16(a, t, b, y, x, c0 + cu * 8, v);
+    if constexpr (TC == 16) {
+      // conv_out: unpatchify + clamp, 4 channels per unit (Cout is not a multiple of 8 here)
+      constexpr int UPR4 = TC / 4;
+      for (int u = tid; u < TP / 2 * UPR4; u += NT) {
+        const int r = u / UPR4, cu4 = u % UPR4;
+        const int p = h * (TP / 2) + r;
+        const int y = Y0 + p / TPX, x = X0 + p % TPX, c = c0 + cu4 * 4;
+        if (y < a.Ho && x < a.Wo && c < a.Cout) {
+          const uint2 w2 = *(const uint2*)(crow(r) + ((cu4 ^ (r & SWZ)) << 3));
+          float v[4] = {bf2f(w2.x & 0xffff), bf2f(w2.x >> 16), bf2f(w2.y & 0xffff), bf2f(w2.y >> 16)};
+          conv_epilogue<T>(a, t, b, y, x, c, v);
+        }
+      }
+    } else {
+      for (int r = tid / UPR; r < TP / 2; r += PSTEP) {
+        const int p = h * (TP / 2) + r;
+        const int y = Y0 + p / TPX, x = X0 + p % TPX;
+        if (y < a.Ho && x < a.Wo) {
+          const char* row = crow(r);
+          const uint2 lo = *(const uint2*)(row + (((2 * cu) ^ (r & SWZ)) << 3));
+          const uint2 hi = *(const uint2*)(row + (((2 * cu + 1) ^ (r & SWZ)) << 3));
+          float v[8];
+          unpack8_bf16(make_uint4(lo.x, lo.y, hi.x, hi.y), v);
+          epilogue8_bf16(a, t, b, y, x, c0 + cu * 8, v);
+        }
       }
     }
   }
@@ -1575,7 +1602,8 @@ static hipError_t conv_dma_go(const ConvArgs& a, hipStream_t s) {
 
 template <int TC, int TPY, int TPX, int WGC, int WGP>
 static hipError_t conv_halo_go(const ConvArgs& a, hipStream_t s) {
-  const int64_t blocks = (int64_t)(a.Cout / TC) * ((a.Wo + TPX - 1) / TPX) * ((a.Ho + TPY - 1) / TPY) * a.F * a.B;
+  const int64_t blocks =
+      (int64_t)((a.Cout + TC - 1) / TC) * ((a.Wo + TPX - 1) / TPX) * ((a.Ho + TPY - 1) / TPY) * a.F * a.B;
   if (a.up)
     hipLaunchKernelGGL((k_conv_halo<TC, TPY, TPX, WGC, WGP, true>), dim3((unsigned)blocks), dim3(64 * WGC * WGP), 0, s, a);
   else
@@ -1584,18 +1612,22 @@ static hipError_t conv_halo_go(const ConvArgs& a, hipStream_t s) {
 }
 
 bool conv_halo_supported(const ConvArgs& a, int dtype, int tile) {
-  const int TC = 128;
-  (void)tile;
-  return dtype == kBF16 && a.kh == 3 && a.kw == 3 && (a.kt == 1 || a.kt == 3) && a.Cin % 32 == 0 &&
-         a.Cout % TC == 0 && a.mode == kEpiFrames && (!a.up || (a.Ho % 2 == 0 && a.Wo % 2 == 0 && a.Hin * 2 == a.Ho &&
-                                                                a.Win * 2 == a.Wo)) &&
-         (a.up || (a.Hin == a.Ho && a.Win == a.Wo));
+  const bool geometry = dtype == kBF16 && a.kh == 3 && a.kw == 3 && (a.kt == 1 || a.kt == 3) && a.Cin % 32 == 0 &&
+                        (!a.up || (a.Ho % 2 == 0 && a.Wo % 2 == 0 && a.Hin * 2 == a.Ho && a.Win * 2 == a.Wo)) &&
+                        (a.up || (a.Hin == a.Ho && a.Win == a.Wo));
+  if (tile == kTileHalo16x16x32)  // conv_out: up to 16 channels, the unpatchify + clamp store
+    return geometry && a.Cout <= 16 && a.Cout % 4 == 0 && a.mode == kEpiVideo;
+  return geometry && a.Cout % 128 == 0 && a.mode == kEpiFrames;
 }
 
 hipError_t launch_conv(const ConvArgs& a, int dtype, int tile, hipStream_t s) {
   if (tile == kTileHalo128x16x32) {
     if (!conv_halo_supported(a, dtype, tile)) return hipErrorInvalidValue;
     return conv_halo_go<128, 16, 32, 2, 4>(a, s);
+  }
+  if (tile == kTileHalo16x16x32) {
+    if (!conv_halo_supported(a, dtype, tile)) return hipErrorInvalidValue;
+    return conv_halo_go<16, 16, 32, 1, 8>(a, s);
   }
   if (dtype == kBF16) {
     if (tile == kTileDma256x128) return conv_dma_go<256, 128, 2, 2, 3, 2>(a, s);

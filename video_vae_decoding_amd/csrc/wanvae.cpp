@@ -341,11 +341,17 @@ static int pick_tile(const ConvArgs& a, int dtype) {
   const int64_t M = (int64_t)a.F * a.B * a.Ho * a.Wo;
   // bf16: the direct-to-LDS kernels (Cout % 8 == 0 for the frame / interleave / q-k-v stores;
   // the unpatchify + clamp store of conv_out on the 16-channel tile)
-  if (dtype == kBF16 && a.mode == kEpiVideo && Cout <= 16 && Cout % 4 == 0) return kTileDma16x256;
+  if (dtype == kBF16 && a.mode == kEpiVideo && Cout <= 16 && Cout % 4 == 0) {
+    // conv_out: the 16-channel halo tile on frames of at least 32 x 64
+    const bool halo16 = conv_halo_supported(a, dtype, kTileHalo16x16x32);
+    if (forced == kTileHalo16x16x32 && halo16) return forced;
+    if (forced == kTileDma16x256) return forced;
+    return halo16 && a.Ho >= 32 && a.Wo >= 64 ? kTileHalo16x16x32 : kTileDma16x256;
+  }
   const bool dma_ok = dtype == kBF16 && a.mode != kEpiVideo && Cout % 8 == 0 && Cout > 64;
   if (!dma_ok) return Cout <= 64 ? kTile32x256 : kTile128x128;
   const bool halo = conv_halo_supported(a, dtype, kTileHalo128x16x32);
-  if (forced >= 0 && (forced != kTileHalo128x16x32 || halo)) return forced;
+  if (forced >= 0 && forced != kTileHalo16x16x32 && (forced != kTileHalo128x16x32 || halo)) return forced;
   // 3x3 convs on frames of at least 32 x 64: the halo tile (input patch shared by the nine
   // spatial taps); 256 x 256 tiles (8 waves of 64 x 128) for the other convs with enough
   // positions to fill the chip; 128 x 128 on the level-0 layers (3,520 positions per frame)
