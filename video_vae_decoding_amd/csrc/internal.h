@@ -73,6 +73,9 @@ struct AttnArgs {
   void* o;         // [nfr][S][C]
   int nfr, S, Sp, C;
   float scale;     // 1/sqrt(C)
+  int ksplit;      // key ranges (> 1: the partial results go to opart / ml, then a combine pass)
+  float* opart;    // [ksplit][nfr][S][C] unnormalised O of each key range
+  float* ml;       // [ksplit][nfr][S][2] running max (base-2 units) and sum of each key range
 };
 
 // Tile shapes of the conv kernel: channels x positions per workgroup.

@@ -1356,6 +1356,9 @@ __global__ void __launch_bounds__(64 * NW) k_attn(const AttnArgs a) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   const int fr = blockIdx.y, q0 = blockIdx.x * 32;
+  // key range of this workgroup: blocks of 32 keys [kb0, kb1) of the frame's ceil(S / 32)
+  const int nkb = (a.S + 31) / 32, kz = blockIdx.z;
+  const int kb0 = (int)((int64_t)nkb * kz / a.ksplit), kb1 = (int)((int64_t)nkb * (kz + 1) / a.ksplit);
   const int C = a.C, S = a.S, Sp = a.Sp;
   const T* Q = (const T*)a.q + (int64_t)fr * S * C;
   const T* K = (const T*)a.k + (int64_t)fr * S * C;
@@ -1377,7 +1380,7 @@ __global__ void __launch_bounds__(64 * NW) k_attn(const AttnArgs a) {
   float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
 
   int par = 0;
-  for (int kv0 = 0; kv0 < S; kv0 += 32, par ^= 1) {
+  for (int kv0 = kb0 * 32; kv0 < kb1 * 32; kv0 += 32, par ^= 1) {
     f32x4_t s[2][2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) s[kt][0] = s[kt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -1474,6 +1477,21 @@ __global__ void __launch_bounds__(64 * NW) k_attn(const AttnArgs a) {
       }
     }
   }
+  if (a.ksplit > 1) {
+    // this key range's unnormalised O and (max, sum): k_attn_combine merges the ranges
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const int qi = q0 + qt * 16 + l16;
+      if (qi >= S) continue;
+      const int64_t row = ((int64_t)kz * a.nfr + fr) * S + qi;
+      float* orow = a.opart + row * C + dw0 + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        *(float4*)(orow + dt * 16) = make_float4(o[dt][qt][0], o[dt][qt][1], o[dt][qt][2], o[dt][qt][3]);
+      if (w == 0 && g == 0) *(float2*)(a.ml + row * 2) = make_float2(mrun[qt], lrun[qt]);
+    }
+    return;
+  }
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
     const int qi = q0 + qt * 16 + l16;
@@ -1488,6 +1506,34 @@ __global__ void __launch_bounds__(64 * NW) k_attn(const AttnArgs a) {
       X::st4(orow + dt * 16, v);
     }
   }
+}
+
+// Key-split finish: O = sum_z 2^(m_z - m) O_z / sum_z 2^(m_z - m) l_z with m = max_z m_z, the
+// ranges taken in order; one thread per 4 head dims of one query.
+template <typename T>
+__global__ void __launch_bounds__(256) k_attn_combine(const AttnArgs a) {
+  using X = Elem<T>;
+  const int C4 = a.C / 4;
+  const int64_t rows = (int64_t)a.nfr * a.S;
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (u >= rows * C4) return;
+  const int64_t row = u / C4;
+  const int d = (int)(u - row * C4) * 4;
+  float m = -INFINITY;
+  for (int z = 0; z < a.ksplit; ++z) m = fmaxf(m, a.ml[(z * rows + row) * 2]);
+  float l = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int z = 0; z < a.ksplit; ++z) {
+    const float2 mlz = *(const float2*)(a.ml + (z * rows + row) * 2);
+    const float wz = exp2f(mlz.x - m);
+    const float4 oz = *(const float4*)(a.opart + (z * rows + row) * a.C + d);
+    l += wz * mlz.y;
+    o[0] += wz * oz.x, o[1] += wz * oz.y, o[2] += wz * oz.z, o[3] += wz * oz.w;
+  }
+  const float inv = 1.f / l;
+  float v[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = o[e] * inv;
+  X::st4((T*)a.o + row * a.C + d, v);
 }
 
 // ------------------------------------------------------------------ small kernels
@@ -1687,7 +1733,13 @@ hipError_t launch_norm(const NormArgs& a, int dtype, hipStream_t s) {
 
 template <typename T, int NW, int DW>
 static hipError_t attn_go(const AttnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((k_attn<T, NW, DW>), dim3((unsigned)((a.S + 31) / 32), (unsigned)a.nfr), dim3(64 * NW), 0, s, a);
+  hipLaunchKernelGGL((k_attn<T, NW, DW>), dim3((unsigned)((a.S + 31) / 32), (unsigned)a.nfr, (unsigned)a.ksplit),
+                     dim3(64 * NW), 0, s, a);
+  if (a.ksplit > 1) {
+    if (hipError_t e = hipGetLastError()) return e;
+    const int64_t units = (int64_t)a.nfr * a.S * (a.C / 4);
+    hipLaunchKernelGGL((k_attn_combine<T>), dim3((unsigned)((units + 255) / 256)), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -485,7 +485,18 @@ struct AttnBufs {
   void *n = nullptr, *q = nullptr, *k = nullptr, *vt = nullptr, *o = nullptr;
   int S = 0, Sp = 0;
   SplitBuf split;  // the standalone block's split-K scratch (the decoder has its own)
+  int ksplit = 1;  // attention key ranges, and their partial results
+  float* opart = nullptr;
+  float* ml = nullptr;
 };
+
+// Attention key ranges: with fewer than 256 workgroups of 32 queries, up to 4 ranges of keys
+// run as separate workgroups (the frames of one chunk would leave most of the chip idle).
+static int attn_split(int nfr, int S) {
+  const int64_t qtiles = (int64_t)nfr * ((S + 31) / 32);
+  if (qtiles >= 256) return 1;
+  return (int)std::min<int64_t>({4, (512 + qtiles - 1) / qtiles, (S + 31) / 32});
+}
 
 static void plan_attn_bufs(Arena& ar, AttnBufs& ab, int nfr, int S, int C, int dtype, bool with_split) {
   const size_t es = esize(dtype);
@@ -497,6 +508,11 @@ static void plan_attn_bufs(Arena& ar, AttnBufs& ab, int nfr, int S, int C, int d
   ab.vt = ar.take((size_t)nfr * C * ab.Sp * es);
   ab.o = ar.take((size_t)nfr * S * C * es);
   if (with_split) ab.split = take_split(ar, (int64_t)nfr * S, 3 * (int64_t)C);
+  ab.ksplit = attn_split(nfr, S);
+  if (ab.ksplit > 1) {
+    ab.opart = (float*)ar.take((size_t)ab.ksplit * nfr * S * C * 4);
+    ab.ml = (float*)ar.take((size_t)ab.ksplit * nfr * S * 2 * 4);
+  }
 }
 
 static int run_attn(const FrameRef& x, const FrameRef& y, int nfr, int H, int W, int C, const float* gamma,
@@ -518,6 +534,7 @@ static int run_attn(const FrameRef& x, const FrameRef& y, int nfr, int H, int W,
   aa.q = ab.q, aa.k = ab.k, aa.vt = ab.vt, aa.o = ab.o;
   aa.nfr = nfr, aa.S = S, aa.Sp = ab.Sp, aa.C = C;
   aa.scale = (float)(1.0 / std::sqrt((double)C));
+  aa.ksplit = ab.ksplit, aa.opart = ab.opart, aa.ml = ab.ml;
   hipEvent_t e0 = prof_start(st);
   HIP_TRY(launch_attn(aa, dtype, st));
   prof_stop(e0, WANVAE_KATTN, 4.0 * nfr * (double)S * S * C, 0, st);
