@@ -92,11 +92,12 @@ enum ConvTile {
   kTileDma256x256w8b = 9,  // 8 waves, 64 x 128 per wave
   kTileHalo128x16x32 = 10, // bf16 3x3 convs: 128 channels x a 16 x 32 block, input patch reused over the taps
   kTileHalo16x16x32 = 11,  // the same for conv_out (up to 16 channels, the video store)
+  kTileHalo128x16x16 = 12, // 128 channels x a 16 x 16 block (small frames, with split K)
 };
 
 hipError_t launch_conv(const ConvArgs& a, int dtype, int tile, hipStream_t s);
 // whether a halo-tile kernel handles this conv (bf16, 3x3 spatial, Cin % 32; tile 10: Cout % 128 and
-// the frame epilogue; tile 11: Cout <= 16 and the video epilogue)
+// the frame epilogue; tile 11: Cout <= 16 and the video epilogue; tile 12 as tile 10)
 bool conv_halo_supported(const ConvArgs& a, int dtype, int tile);
 hipError_t launch_norm(const NormArgs& a, int dtype, hipStream_t s);
 bool attn_supported(int C, int dtype);

@@ -935,7 +935,11 @@ __global__ void __launch_bounds__(64 * WGC * WGP, 1) k_conv_halo(const ConvArgs 
   const int tiles_x = (a.Wo + TPX - 1) / TPX, tiles_y = (a.Ho + TPY - 1) / TPY;
   // block coordinates are wave-uniform: keep them scalar so that the frame tables are read
   // with scalar loads
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  // split K: workgroup range kz of a.ksplit takes the kz-th contiguous range of step groups
+  const int ntiles = nct * tiles_x * tiles_y * a.F * a.B;
+  const int bid0 = xcd_remap(blockIdx.x, gridDim.x);
+  const int kz = __builtin_amdgcn_readfirstlane(bid0 / ntiles);
+  const int bid = bid0 - kz * ntiles;
   const int ct = __builtin_amdgcn_readfirstlane(bid % nct);
   int rem = __builtin_amdgcn_readfirstlane(bid / nct);
   const int tx = __builtin_amdgcn_readfirstlane(rem % tiles_x);
@@ -945,7 +949,10 @@ __global__ void __launch_bounds__(64 * WGC * WGP, 1) k_conv_halo(const ConvArgs 
   const int b = __builtin_amdgcn_readfirstlane(rem % a.B), t = __builtin_amdgcn_readfirstlane(rem / a.B);
   const int c0 = ct * TC, Y0 = ty * TPY, X0 = tx * TPX;
   const int csteps = a.Cin / 32;
-  const int G = a.kt * csteps;  // step groups: (time tap, channel block), nine spatial taps each
+  // step groups: (time tap, channel block), nine spatial taps each; this workgroup's range
+  const int G_all = a.kt * csteps;
+  const int g_begin = (int)((int64_t)G_all * kz / a.ksplit);
+  const int G = (int)((int64_t)G_all * (kz + 1) / a.ksplit) - g_begin;
   const int S = 9 * G;
   const int64_t Ktot = (int64_t)a.kt * 9 * a.Cin;
   const char* zero = (const char*)g_zero_page;
@@ -1008,7 +1015,8 @@ __global__ void __launch_bounds__(64 * WGC * WGP, 1) k_conv_halo(const ConvArgs 
   };
   // cursors over the step groups (channel block minor, time tap major), advanced without
   // divisions: (dt1, cb1) names the group after the current one, (dt2, cb2) the one after that
-  int dt1 = 0, cb1 = 0, dt2 = 0, cb2 = 0;
+  const int dt0 = g_begin / csteps, cb0 = (g_begin - dt0 * csteps) * 32;  // the range's first group
+  int dt1 = dt0, cb1 = cb0, dt2 = dt0, cb2 = cb0;
   const char* fb2p = fb0;
   auto step_group = [&](int& dt, int& cb) {
     cb += 32;
@@ -1083,11 +1091,12 @@ __global__ void __launch_bounds__(64 * WGC * WGP, 1) k_conv_halo(const ConvArgs 
   // patch any more, and step s + 1's fragments are read into the other register set between
   // step s's MFMAs.
   char* wb[9] = {w0, w1, w2, w3, w4, w5, w6, w7, w8};
-  issue_p(p0, fb0, 0);
+  const int wofs0 = (dt0 * 9 * Cin + cb0) * 2;
+  issue_p(p0, frame_of(dt0), cb0 * 2);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) issue_w(wb[j], 0, j, true);
+  for (int j = 0; j < 8; ++j) issue_w(wb[j], wofs0, j, true);
   sync_step(0);
-  issue_w(wb[8], 0, 8, true);
+  issue_w(wb[8], wofs0, 8, true);
   issue_p(p1, frame_of(dt1), cb1 * 2);
   __builtin_amdgcn_sched_barrier(0);
   read_frags(0, wb[0], p0, 0);
@@ -1131,10 +1140,29 @@ __global__ void __launch_bounds__(64 * WGC * WGP, 1) k_conv_halo(const ConvArgs 
     }
   }
 
+  wait_vm_lgkm0<0>();
+  if (a.ksplit > 1) {
+    // split K: the raw float32 sums of this range go to the partials buffer [ksplit][M][Cout]
+    // (position m = ((t * B + b) * Ho + y) * Wo + x); k_splitk_reduce finishes them
+    const int64_t M = (int64_t)a.F * a.B * a.Ho * a.Wo;
+#pragma unroll
+    for (int ip = 0; ip < TPN; ++ip) {
+      const int p = wp * WP + ip * 16 + (lane & 15);
+      const int y = Y0 + p / TPX, x = X0 + p % TPX;
+      const int64_t m = (((int64_t)t * a.B + b) * a.Ho + y) * a.Wo + x;
+#pragma unroll
+      for (int ic = 0; ic < TCN; ++ic) {
+        const int c = c0 + wc * WC + ic * 16 + 4 * (lane >> 4);
+        if (y < a.Ho && x < a.Wo && c < a.Cout)
+          *(float4*)(a.part + ((int64_t)kz * M + m) * a.Cout + c) =
+              make_float4(acc[ic][ip][0], acc[ic][ip][1], acc[ic][ip][2], acc[ic][ip][3]);
+      }
+    }
+    return;
+  }
   // Epilogue in two passes of half the positions, staged in the patch buffers (rows of TC
   // bf16 channels, 8-byte slots permuted by slot ^ (row & 15)); 8-channel units are then
   // finished and stored with 16-byte accesses.
-  wait_vm_lgkm0<0>();
   constexpr int SWZ = TC / 4 - 1 < 15 ? TC / 4 - 1 : 15;
   auto crow = [&](int r) -> char* { return r < RPA ? p0 + r * RB : p1 + (r - RPA) * RB; };
   float4 bias[TCN];  // (Cout is a multiple of 4: a lane's 4 channels all exist or all do not)
@@ -1649,12 +1677,18 @@ static hipError_t conv_dma_go(const ConvArgs& a, hipStream_t s) {
 template <int TC, int TPY, int TPX, int WGC, int WGP>
 static hipError_t conv_halo_go(const ConvArgs& a, hipStream_t s) {
   const int64_t blocks =
-      (int64_t)((a.Cout + TC - 1) / TC) * ((a.Wo + TPX - 1) / TPX) * ((a.Ho + TPY - 1) / TPY) * a.F * a.B;
+      (int64_t)((a.Cout + TC - 1) / TC) * ((a.Wo + TPX - 1) / TPX) * ((a.Ho + TPY - 1) / TPY) * a.F * a.B * a.ksplit;
   if (a.up)
     hipLaunchKernelGGL((k_conv_halo<TC, TPY, TPX, WGC, WGP, true>), dim3((unsigned)blocks), dim3(64 * WGC * WGP), 0, s, a);
   else
     hipLaunchKernelGGL((k_conv_halo<TC, TPY, TPX, WGC, WGP, false>), dim3((unsigned)blocks), dim3(64 * WGC * WGP), 0, s, a);
-  return hipGetLastError();
+  if (hipError_t e = hipGetLastError()) return e;
+  if (a.ksplit > 1) {
+    const int64_t units = (int64_t)a.F * a.B * a.Ho * a.Wo * (a.Cout / 8);
+    hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 bool conv_halo_supported(const ConvArgs& a, int dtype, int tile) {
@@ -1674,6 +1708,10 @@ hipError_t launch_conv(const ConvArgs& a, int dtype, int tile, hipStream_t s) {
   if (tile == kTileHalo16x16x32) {
     if (!conv_halo_supported(a, dtype, tile)) return hipErrorInvalidValue;
     return conv_halo_go<16, 16, 32, 1, 8>(a, s);
+  }
+  if (tile == kTileHalo128x16x16) {
+    if (!conv_halo_supported(a, dtype, tile)) return hipErrorInvalidValue;
+    return conv_halo_go<128, 16, 16, 2, 4>(a, s);
   }
   if (dtype == kBF16) {
     if (tile == kTileDma256x128) return conv_dma_go<256, 128, 2, 2, 3, 2>(a, s);

@@ -351,11 +351,14 @@ static int pick_tile(const ConvArgs& a, int dtype) {
   const bool dma_ok = dtype == kBF16 && a.mode != kEpiVideo && Cout % 8 == 0 && Cout > 64;
   if (!dma_ok) return Cout <= 64 ? kTile32x256 : kTile128x128;
   const bool halo = conv_halo_supported(a, dtype, kTileHalo128x16x32);
-  if (forced >= 0 && forced != kTileHalo16x16x32 && (forced != kTileHalo128x16x32 || halo)) return forced;
+  const bool forced_halo = forced == kTileHalo128x16x32 || forced == kTileHalo128x16x16;
+  if (forced >= 0 && forced != kTileHalo16x16x32 && (!forced_halo || halo)) return forced;
   // 3x3 convs on frames of at least 32 x 64: the halo tile (input patch shared by the nine
-  // spatial taps); 256 x 256 tiles (8 waves of 64 x 128) for the other convs with enough
-  // positions to fill the chip; 128 x 128 on the level-0 layers (3,520 positions per frame)
-  if (halo && a.Ho >= 32 && a.Wo >= 64 && M >= 16384) return kTileHalo128x16x32;
+  // spatial taps), 16 x 32 blocks, or 16 x 16 blocks with split K where the frames leave
+  // the chip short of blocks (the level-0 layers: 3,520 positions per frame); 256 x 256
+  // tiles (8 waves of 64 x 128) for the other convs with enough positions to fill the chip;
+  // 128 x 128 (with split K) for the rest
+  if (halo && a.Ho >= 32 && a.Wo >= 64) return M >= 16384 ? kTileHalo128x16x32 : kTileHalo128x16x16;
   if (M < 16384) return kTileDma128x128;
   return Cout % 256 == 0 ? kTileDma256x256w8b : kTileDma256x128;
 }
@@ -387,22 +390,32 @@ static SplitBuf take_split(Arena& ar, int64_t M, int64_t Cout) {
 // K split of a direct-to-LDS conv: enough workgroups for about three per CU when the tiles
 // alone leave the chip short, at least 16 K steps per range, within the partials scratch.
 static int split_for(const ConvArgs& a, int tile, int dtype, const SplitBuf& sb) {
-  int TC = 0, TP = 0;
+  int TC = 0, TP = 0, TPY = 0, TPX = 0;
   switch (tile) {
     case kTileDma256x128: TC = 256, TP = 128; break;
     case kTileDma256x256: case kTileDma256x256w8: case kTileDma256x256w8b: TC = 256, TP = 256; break;
     case kTileDma128x128: TC = 128, TP = 128; break;
     case kTileDma128x256: TC = 128, TP = 256; break;
     case kTileDma16x256: TC = 16, TP = 256; break;
+    case kTileHalo128x16x32: TC = 128, TPY = 16, TPX = 32; break;
+    case kTileHalo128x16x16: TC = 128, TPY = 16, TPX = 16; break;
     default: return 1;
   }
   if (dtype != kBF16 || a.mode == kEpiVideo || a.Cout % 8 || sb.p == nullptr) return 1;
   const int64_t M = (int64_t)a.F * a.B * a.Ho * a.Wo;
-  const int64_t tiles = ((a.Cout + TC - 1) / TC) * ((M + TP - 1) / TP);
-  const int steps = a.kt * a.kh * a.kw * ((a.Cin + 31) / 32);
+  const int64_t nct = (a.Cout + TC - 1) / TC;
+  // tiles, and the K units a range must hold: 16 steps of 32 channels, or (halo tile) 4 groups
+  // of nine taps
+  int64_t tiles, units;
+  if (TPX) {
+    tiles = nct * ((a.Ho + TPY - 1) / TPY) * ((a.Wo + TPX - 1) / TPX) * a.F * a.B;
+    units = a.kt * (a.Cin / 32) / 4;
+  } else {
+    tiles = nct * ((M + TP - 1) / TP);
+    units = a.kt * a.kh * a.kw * ((a.Cin + 31) / 32) / 16;
+  }
   if (tiles >= 512) return 1;
-  int ks = (int)std::min<int64_t>(4, (768 + tiles - 1) / tiles);
-  ks = std::min(ks, steps / 16);
+  int ks = (int)std::min<int64_t>({4, (768 + tiles - 1) / tiles, units});
   while (ks > 1 && (size_t)ks * M * a.Cout > sb.floats) --ks;
   return std::max(ks, 1);
 }
