@@ -12,8 +12,13 @@ bf16 dense MFMA peak; the HBM bytes per launch from the stored counter measureme
 kernel source it was taken on is unchanged), the other kernel classes, and the CPU oracle
 timed on a bounded sample.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--workload NAME]
     python bench.py --copy-bytes N    # three device-to-device copies of N bytes (counter scale)
+
+--workload picks another of the measured configurations (default ti2v5b_landscape_bf16):
+ti2v5b_landscape_fp32, ti2v5b_portrait_bf16, ti2v5b_landscape_b2_bf16 (whole decodes, frames/s),
+conv1024_l0_bf16, conv256_l3_bf16 (one causal conv, TFLOP/s), attn1024_31f_bf16 (the attention
+block over 31 frames, TFLOP/s).
 """
 import argparse
 import hashlib
@@ -39,23 +44,24 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(cfg, W):
-    """The CPU oracle (as it stands: float64 sums, bf16 rounding points) decoding the first
-    latent frame of the same decoder on an 11 x 20 crop of the latent (1/16 of the 44 x 80
-    frame area: 1/16 of a video frame's work, attention aside), scaled to full frames/s."""
+def cpu_baseline(cfg, W, mode="bf16"):
+    """The CPU oracle (as it stands: float64 sums, the mode's rounding points) decoding the
+    first latent frame of the same decoder on a crop of the latent with 1/16 of the frame area
+    (1/16 of a video frame's work, attention aside), scaled to full frames/s."""
     import oracle
-    z = cfg.latents()[:, :, :1, :11, :20]
+    ch, cw = (11, 20) if cfg.h <= cfg.w else (20, 11)
+    z = cfg.latents()[:1, :, :1, :ch, :cw]
     t0 = time.perf_counter()
-    v = oracle.decode(np.ascontiguousarray(z), W, "bf16")
+    v = oracle.decode(np.ascontiguousarray(z), W, mode)
     dt = time.perf_counter() - t0
-    frac = (11 * 20) / (cfg.h * cfg.w)
+    frac = (ch * cw) / (cfg.h * cfg.w)
     cores = len(os.sched_getaffinity(0))
     threads = os.environ.get("OPENBLAS_NUM_THREADS") or os.environ.get("OMP_NUM_THREADS") or str(cores)
     return {"value": frac * v.shape[2] / dt, "unit": "frames/s", "cores": int(threads) if threads.isdigit() else cores,
             "kind": "oracle", "seconds": round(dt, 2),
-            "sample": "oracle.decode (bf16 mode, float64 sums) of latent frame 0 on an 11x20 crop of the "
-                      "[1,48,31,44,80] latents: 1 video frame of 176x320 = 1/16 of a 704x1280 frame; "
-                      "value = (1/16 frame) / seconds"}
+            "sample": f"oracle.decode ({mode} mode, float64 sums) of latent frame 0 on a {ch}x{cw} crop of the "
+                      f"[{cfg.B},48,{cfg.T},{cfg.h},{cfg.w}] latents (batch element 0): 1 video frame of "
+                      f"{16 * ch}x{16 * cw} = 1/16 of a {16 * cfg.h}x{16 * cfg.w} frame; value = (1/16 frame) / seconds"}
 
 
 def stored_traffic():
@@ -83,6 +89,85 @@ def copy_calibration(nbytes):
     print(json.dumps({"copy_bytes": nbytes, "copies": 3}), flush=True)
 
 
+DECODES = {"ti2v5b_landscape_bf16": ("ti2v5b_landscape", "bf16"), "ti2v5b_landscape_fp32": ("ti2v5b_landscape", "fp32"),
+           "ti2v5b_portrait_bf16": ("ti2v5b_portrait", "bf16"), "ti2v5b_landscape_b2_bf16": ("ti2v5b_landscape_b2", "bf16")}
+SINGLE = {"conv1024_l0_bf16": ("conv", "conv1024_l0"), "conv256_l3_bf16": ("conv", "conv256_l3"),
+          "attn1024_31f_bf16": ("attn", "attn1024_31f")}
+
+
+def kernel_classes(prof, steps):
+    out = {}
+    for k, p in prof.items():
+        e = {"ms_per_step": round(p["ms"] / steps, 3), "launches_per_step": p["launches"] // max(1, steps)}
+        if p["flops"]:
+            e["TFLOP/s"] = round(p["flops"] / (p["ms"] * 1e-3) / 1e12, 2)
+        if p["bytes"]:
+            e["GB/s"] = round(p["bytes"] / (p["ms"] * 1e-3) / 1e9, 1)
+            e["frac_of_peak"] = round(e["GB/s"] / PEAK_HBM_GBS, 4)
+        out[k] = e
+    return out
+
+
+def single_op(name, args):
+    """One causal conv (C2a, C2b) or the attention block (C3) in bf16, NTHWC operands resident
+    in HBM; value = the op's algorithmic TFLOP/s over the timed wall time."""
+    import torch
+
+    import synthetic
+    from video_vae_decoding_amd import wanvae
+    kind, cfg_name = SINGLE[name]
+    dev = torch.device("cuda:0")
+    bf = torch.bfloat16
+    if kind == "conv":
+        cfg = synthetic.CONV_CONFIGS[cfg_name]
+        x, cache, w, b = cfg.tensors()
+        xt = torch.from_numpy(x).to(dev).to(bf).permute(0, 2, 3, 4, 1).contiguous()
+        ct = torch.from_numpy(cache).to(dev).to(bf).permute(0, 2, 3, 4, 1).contiguous()
+        wt, bt = torch.from_numpy(w).to(dev), torch.from_numpy(b).to(dev)
+        y = torch.empty(1, cfg.t, cfg.h, cfg.w, cfg.C, dtype=bf, device=dev)
+        ws = torch.empty(wanvae.conv_workspace_size(1, cfg.C, cfg.C, cfg.t, cfg.h, cfg.w, cfg.n_cache, "nthwc", bf),
+                         dtype=torch.uint8, device=dev)
+        run = lambda: wanvae.wanvae_causal_conv3d(xt, ct, wt, bt, layout="nthwc", y=y, workspace=ws)
+        flops = 2.0 * cfg.t * cfg.h * cfg.w * cfg.C * cfg.C * 27
+        config = {"workload": name, "x": [1, cfg.C, cfg.t, cfg.h, cfg.w], "n_cache": cfg.n_cache, "kernel": "3x3x3"}
+    else:
+        cfg = synthetic.ATTN_CONFIGS[cfg_name]
+        T = cfg.tensors()
+        xt = torch.from_numpy(T["x"]).to(dev).to(bf).permute(0, 2, 3, 4, 1).contiguous()
+        par = [torch.from_numpy(T[k]).to(dev) for k in ("gamma", "qkv_w", "qkv_b", "proj_w", "proj_b")]
+        y = torch.empty_like(xt)
+        ws = torch.empty(wanvae.attn_workspace_size(1, cfg.C, cfg.T, cfg.h, cfg.w, "nthwc", bf), dtype=torch.uint8,
+                         device=dev)
+        run = lambda: wanvae.wanvae_attn_block(xt, *par, layout="nthwc", y=y, workspace=ws)
+        S = cfg.h * cfg.w
+        flops = cfg.T * (4.0 * S * S * cfg.C + 2.0 * S * cfg.C * 4 * cfg.C)  # core + q-k-v and output projections
+        config = {"workload": name, "x": [1, cfg.C, cfg.T, cfg.h, cfg.w], "S": S, "heads": 1}
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    wanvae.wanvae_profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    prof = {k: wanvae.wanvae_profile_read(getattr(wanvae, "K" + k.upper())) for k in ("conv", "norm", "attn", "other")}
+    wanvae.wanvae_profile_enable(False)
+    main_k = prof["conv" if kind == "conv" else "attn"]
+    tf = main_k["flops"] / (main_k["ms"] * 1e-3) / 1e12
+    out = {"metric": f"{'conv' if kind == 'conv' else 'attention block'} TFLOP/s (bf16)",
+           "value": round(flops * args.steps / elapsed / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(elapsed / args.steps * 1e3, 3),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": config,
+           "roofline": {"bound": "mfma", "kernel": "conv" if kind == "conv" else "attention core (k_attn)",
+                        "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                        "launches": main_k["launches"], "avg_launch_ms": round(main_k["ms"] / max(1, main_k["launches"]), 4)},
+           "kernels": kernel_classes(prof, args.steps)}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -90,6 +175,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0)
+    ap.add_argument("--workload", default="ti2v5b_landscape_bf16", choices=sorted(DECODES) + sorted(SINGLE))
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the decoder here runs on a single MI355X (got --gpus {args.gpus}); "
@@ -98,6 +184,9 @@ def main():
     if args.copy_bytes:
         copy_calibration(args.copy_bytes)
         return
+    if args.workload in SINGLE:
+        single_op(args.workload, args)
+        return
 
     import torch
 
@@ -105,12 +194,14 @@ def main():
     from video_vae_decoding_amd import wanvae
 
     dev = torch.device("cuda:0")
-    cfg = synthetic.DECODE_CONFIGS["ti2v5b_landscape"]
+    cfg_name, mode = DECODES[args.workload]
+    cfg = synthetic.DECODE_CONFIGS[cfg_name]
     log("generating inputs ...")
     z, W = cfg.latents(), cfg.weights()
     zt = torch.from_numpy(z).to(dev)
     Wt = {k: torch.from_numpy(v).to(dev) for k, v in W.items()}
-    dtype = torch.bfloat16
+    dtype = torch.bfloat16 if mode == "bf16" else torch.float32
+    peak = PEAK_BF16_TFLOPS if mode == "bf16" else PEAK_FP32_TFLOPS
     frames = cfg.B * cfg.frames
     video = torch.empty((cfg.B, 3, cfg.frames, 16 * cfg.h, 16 * cfg.w), dtype=dtype, device=dev)
     ws = torch.empty(wanvae.decode_workspace_size(cfg.B, cfg.T, cfg.h, cfg.w, Wt, dtype), dtype=torch.uint8, device=dev)
@@ -133,18 +224,13 @@ def main():
 
     conv = prof["conv"]
     conv_tflops = conv["flops"] / (conv["ms"] * 1e-3) / 1e12
-    kernels = {}
-    for k, p in prof.items():
-        e = {"ms_per_step": round(p["ms"] / args.steps, 3), "launches_per_step": p["launches"] // max(1, args.steps)}
-        if p["flops"]:
-            e["TFLOP/s"] = round(p["flops"] / (p["ms"] * 1e-3) / 1e12, 2)
-            e["frac_of_peak"] = round(e["TFLOP/s"] / PEAK_BF16_TFLOPS, 4)
-        if p["bytes"]:
-            e["GB/s"] = round(p["bytes"] / (p["ms"] * 1e-3) / 1e9, 1)
-            e["frac_of_peak"] = round(e["GB/s"] / PEAK_HBM_GBS, 4)
-        kernels[k] = e
+    kernels = kernel_classes(prof, args.steps)
+    for k in ("conv", "attn"):
+        if "TFLOP/s" in kernels[k]:
+            kernels[k]["frac_of_peak"] = round(kernels[k]["TFLOP/s"] / peak, 4)
+    default = args.workload == "ti2v5b_landscape_bf16"
     out = {
-        "metric": METRIC,
+        "metric": METRIC if default else METRIC.replace("704x1280 bf16", f"{16 * cfg.h}x{16 * cfg.w} {mode}"),
         "value": round(frames * args.steps / elapsed, 3),
         "unit": "frames/s",
         "n_gpus": 1,
@@ -154,22 +240,24 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": mode,
         "data": "synthetic",
-        "config": {"workload": "ti2v5b_vae_decode_704x1280x121_bf16", "latent": [cfg.B, 48, cfg.T, cfg.h, cfg.w],
-                   "video": [cfg.B, 3, cfg.frames, 16 * cfg.h, 16 * cfg.w], "weights": "random-init, seed 3",
+        "config": {"workload": f"ti2v5b_vae_decode_{16 * cfg.h}x{16 * cfg.w}x{cfg.frames}_{mode}" + ("" if cfg.B == 1 else f"_b{cfg.B}"),
+                   "latent": [cfg.B, 48, cfg.T, cfg.h, cfg.w],
+                   "video": [cfg.B, 3, cfg.frames, 16 * cfg.h, 16 * cfg.w], "weights": f"random-init, seed {cfg.seed}",
                    "accumulate": "fp32"},
         "roofline": {"bound": "mfma",
-                     "kernel": "conv (k_conv_halo for the 3x3 convs, k_conv_dma for the rest; all launches of a decode)",
-                     "achieved": round(conv_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(conv_tflops / PEAK_BF16_TFLOPS, 4), "traffic": stored_traffic(),
+                     "kernel": ("conv (k_conv_halo for the 3x3 convs, k_conv_dma for the rest; all launches of a decode)"
+                                if mode == "bf16" else "conv (k_conv, fp32 MFMA; all launches of a decode)"),
+                     "achieved": round(conv_tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(conv_tflops / peak, 4), "traffic": stored_traffic() if default else None,
                      "launches": conv["launches"], "avg_launch_ms": round(conv["ms"] / max(1, conv["launches"]), 4),
                      "algorithmic_tflop_per_step": round(conv["flops"] / args.steps / 1e12, 2)},
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on its sample ...")
-        out["cpu_baseline"] = cpu_baseline(cfg, W)
+        out["cpu_baseline"] = cpu_baseline(cfg, W, mode)
     print(json.dumps(out), flush=True)
 
 
