@@ -18,7 +18,8 @@ timed on a bounded sample.
 --workload picks another of the measured configurations (default ti2v5b_landscape_bf16):
 ti2v5b_landscape_fp32, ti2v5b_portrait_bf16, ti2v5b_landscape_b2_bf16 (whole decodes, frames/s),
 conv1024_l0_bf16, conv256_l3_bf16 (one causal conv, TFLOP/s), attn1024_31f_bf16 (the attention
-block over 31 frames, TFLOP/s).
+block over 31 frames, TFLOP/s), attn384_s14400_21f_bf16 and attn1024_s14400_21f_bf16 (the block
+over 21 frames of the Wan2.1 720p latent, 90x160 positions, at widths 384 and 1024).
 """
 import argparse
 import hashlib
@@ -92,7 +93,8 @@ def copy_calibration(nbytes):
 DECODES = {"ti2v5b_landscape_bf16": ("ti2v5b_landscape", "bf16"), "ti2v5b_landscape_fp32": ("ti2v5b_landscape", "fp32"),
            "ti2v5b_portrait_bf16": ("ti2v5b_portrait", "bf16"), "ti2v5b_landscape_b2_bf16": ("ti2v5b_landscape_b2", "bf16")}
 SINGLE = {"conv1024_l0_bf16": ("conv", "conv1024_l0"), "conv256_l3_bf16": ("conv", "conv256_l3"),
-          "attn1024_31f_bf16": ("attn", "attn1024_31f")}
+          "attn1024_31f_bf16": ("attn", "attn1024_31f"), "attn384_s14400_21f_bf16": ("attn", "attn384_s14400_21f"),
+          "attn1024_s14400_21f_bf16": ("attn", "attn1024_s14400_21f")}
 
 
 def kernel_classes(prof, steps):

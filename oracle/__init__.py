@@ -30,6 +30,7 @@ from .decoder import (  # noqa: F401
     MODES,
     Prec,
     attention,
+    attention_rows,
     cached_conv,
     causal_conv,
     conv_points,

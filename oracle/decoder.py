@@ -239,6 +239,31 @@ def attention(x, gamma, qkv_w, qkv_b, proj_w, proj_b, P: Prec) -> np.ndarray:
     return out
 
 
+def attention_rows(frame, gamma, qkv_w, qkv_b, proj_w, proj_b, P: Prec, rows) -> np.ndarray:
+    """The attention block of one frame [C, H, W] at the query positions ``rows`` (indices
+    into the row-major H*W sequence): the same steps as ``attention``, with the scores and
+    outputs computed only for those queries (every key and value is still used). Returns
+    [len(rows), C]; for frames too large for the full score matrix."""
+    C, H, W = frame.shape
+    S = H * W
+    rows = np.asarray(rows)
+    wq = np.asarray(qkv_w).reshape(3 * C, C).astype(P.acc_t)
+    wp = np.asarray(proj_w).reshape(C, C).astype(P.acc_t)
+    bq = np.asarray(qkv_b, P.acc_t)
+    n = rms_norm(frame[None], gamma, P)[0]
+    seq = n.reshape(C, S).T.astype(P.acc_t)                              # [S, C]
+    k = P.R(seq @ wq[C:2 * C].T + bq[C:2 * C]).astype(np.float64)
+    v = P.R(seq @ wq[2 * C:].T + bq[2 * C:]).astype(np.float64)
+    q = P.R(seq[rows] @ wq[:C].T + bq[:C]).astype(np.float64)
+    s = (q @ k.T) * (1.0 / math.sqrt(C))
+    s -= s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    p /= p.sum(axis=1, keepdims=True)
+    o = P.R(p @ v)
+    y = P.R(o.astype(P.acc_t) @ wp.T + np.asarray(proj_b, P.acc_t))
+    return P.R(y.astype(np.float64) + frame.reshape(C, S).T[rows].astype(np.float64))
+
+
 def time_upsample(x, Wt, name, cache, P: Prec) -> np.ndarray:
     """upsample3d's time conv: a causal 3x1x1 conv C -> 2C whose output channel c becomes
     frame 2t and channel C + c frame 2t + 1 ("The parts": upsample3d)."""

@@ -188,4 +188,14 @@ class AttnConfig:
         }
 
 
-ATTN_CONFIGS = {"attn1024_31f": AttnConfig("attn1024_31f", 1024, 31, 44, 80, 2)}
+# attn1024_31f: the TI2V-5B mid block over 31 latent frames of 44x80. The *_s14400 configs:
+# the Wan2.1 720p latent frame (90x160 = 14,400 positions per frame), with the block width a
+# parameter (384, Wan2.1's mid-block width, and 1024): 2 frames for the parity tests, 21 (81
+# video frames) for the measurement.
+ATTN_CONFIGS = {
+    "attn1024_31f": AttnConfig("attn1024_31f", 1024, 31, 44, 80, 2),
+    "attn384_s14400": AttnConfig("attn384_s14400", 384, 2, 90, 160, 5),
+    "attn1024_s14400": AttnConfig("attn1024_s14400", 1024, 2, 90, 160, 6),
+    "attn384_s14400_21f": AttnConfig("attn384_s14400_21f", 384, 21, 90, 160, 5),
+    "attn1024_s14400_21f": AttnConfig("attn1024_s14400_21f", 1024, 21, 90, 160, 6),
+}

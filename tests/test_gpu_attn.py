@@ -93,3 +93,38 @@ def test_attn_full_size_sampled_frames(mode):
     for f in (0, 17, 30):
         got = to_np(y[:, f:f + 1]).transpose(0, 4, 1, 2, 3)
         compare(got, x[:, :, f:f + 1], ws, mode, f"frame {f} {mode}")
+
+
+@pytest.mark.parametrize("mode", ["bf16", "fp32"])
+@pytest.mark.parametrize("name", ["attn384_s14400", "attn1024_s14400"])
+def test_attn_720p_frames_sampled_rows(name, mode):
+    """The Wan2.1 720p latent frame (S = 14,400 positions, 2 frames): 384 seeded query
+    positions per frame against the oracle's block at those queries (every key used)."""
+    cfg = synthetic.ATTN_CONFIGS[name]
+    say("attn 720p", name, mode)
+    t = cfg.tensors()
+    x = t["x"]
+    ws = [t[k] for k in ("gamma", "qkv_w", "qkv_b", "proj_w", "proj_b")]
+    xt = to_dev(x, mode).permute(0, 2, 3, 4, 1).contiguous()
+    y = wanvae.wanvae_attn_block(xt, *[to_dev(a, mode) for a in ws], layout="nthwc")
+    torch.cuda.synchronize()
+    S, C = cfg.h * cfg.w, cfg.C
+    rows = np.sort(np.random.default_rng(20251202).choice(S, 384, replace=False))
+    P = oracle.Prec(mode)
+    xr = rounded(x, mode)
+    wr = [rounded(a, mode) for a in ws]
+    for f in range(cfg.T):
+        got = to_np(y[0, f].reshape(S, C)[torch.from_numpy(rows).to(y.device)])
+        want = oracle.attention_rows(xr[0, :, f], *wr, P, rows)
+        xrows = xr[0, :, f].reshape(C, S).T[rows]
+        d = np.abs(got.astype(np.float64) - want)
+        br = want - xrows
+        rel = np.linalg.norm(got - want) / np.linalg.norm(br)
+        say(name, mode, "frame", f, "max", d.max(), "branch rel", rel)
+        if mode == "fp32":
+            assert d.max() <= 1e-4 * max(1.0, np.abs(br).max()), d.max()
+            assert rel <= 1e-5
+        else:
+            lim = np.maximum(3e-2, 2 * bf16_ulp(np.abs(want)))
+            assert np.all(d <= lim), d.max()
+            assert rel <= 1.5e-2, rel

@@ -289,6 +289,35 @@ def test_attention_zero_queries_average_values():
     np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("mode", ["fp64", "fp32", "bf16"])
+def test_attention_rows_equals_the_full_block_at_those_rows(mode):
+    """attention_rows (queries restricted to a subset of positions) gives the full block's
+    outputs at those positions: the same values, up to the summation order of the row
+    subset's matrix products (a bf16 rounding may then flip by one spacing)."""
+    g = np.random.default_rng(11)
+    C, H, W = 32, 5, 7
+    x = g.standard_normal((1, C, 1, H, W))
+    gm = 1 + 0.1 * g.standard_normal((C, 1, 1))
+    wq = g.standard_normal((3 * C, C, 1, 1)) / np.sqrt(C)
+    bq = g.standard_normal(3 * C) / np.sqrt(C)
+    wp = g.standard_normal((C, C, 1, 1)) / np.sqrt(C)
+    bp = g.standard_normal(C) / np.sqrt(C)
+    P = oracle.Prec(mode)
+    if mode != "fp64":
+        x, gm, wq, bq, wp, bp = (P.R(a) for a in (x, gm, wq, bq, wp, bp))
+    full = oracle.attention(x, gm, wq, bq, wp, bp, P)[0, :, 0].reshape(C, H * W).T
+    rows = np.array([0, 3, 17, 34, 20, 9])
+    got = oracle.attention_rows(x[0, :, 0], gm, wq, bq, wp, bp, P, rows)
+    assert got.shape == (len(rows), C)
+    if mode == "fp64":
+        np.testing.assert_allclose(got, full[rows], rtol=1e-12, atol=1e-12)
+    else:
+        d = np.abs(got - full[rows])
+        spacing = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(full[rows]), 1e-30))) - (7 if mode == "bf16" else 23))
+        assert np.all(d <= spacing), d.max()
+        assert np.mean(d == 0) >= 0.99
+
+
 def test_attention_matches_torch_sdpa():
     """q, k, v from the (N*T, H*W, 1, C) layout through torch's scaled_dot_product_attention
     in float64, one head of dim C."""

@@ -1783,7 +1783,7 @@ static hipError_t attn_go(const AttnArgs& a, hipStream_t s) {
 
 bool attn_supported(int C, int dtype) {
   (void)dtype;
-  return C == 64 || C == 128 || C == 256 || C == 512 || C == 1024;
+  return C == 64 || C == 128 || C == 256 || C == 384 || C == 512 || C == 1024;
 }
 
 hipError_t launch_attn(const AttnArgs& a, int dtype, hipStream_t s) {
@@ -1792,6 +1792,7 @@ hipError_t launch_attn(const AttnArgs& a, int dtype, hipStream_t s) {
       case 64: return attn_go<bf16_t, 2, 32>(a, s);
       case 128: return attn_go<bf16_t, 4, 32>(a, s);
       case 256: return attn_go<bf16_t, 4, 64>(a, s);
+      case 384: return attn_go<bf16_t, 4, 96>(a, s);
       case 512: return attn_go<bf16_t, 4, 128>(a, s);
       case 1024: return attn_go<bf16_t, 4, 256>(a, s);
     }
@@ -1800,6 +1801,7 @@ hipError_t launch_attn(const AttnArgs& a, int dtype, hipStream_t s) {
       case 64: return attn_go<float, 4, 16>(a, s);
       case 128: return attn_go<float, 8, 16>(a, s);
       case 256: return attn_go<float, 8, 32>(a, s);
+      case 384: return attn_go<float, 8, 48>(a, s);
       case 512: return attn_go<float, 8, 64>(a, s);
       case 1024: return attn_go<float, 8, 128>(a, s);
     }
