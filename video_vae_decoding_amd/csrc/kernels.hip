@@ -1746,7 +1746,7 @@ hipError_t launch_norm(const NormArgs& a, int dtype, hipStream_t s) {
       case 64: return norm_v_go<bf16_t, 8, 1>(a, s);
       case 128: return norm_v_go<bf16_t, 16, 1>(a, s);
       case 256: return norm_v_go<bf16_t, 32, 1>(a, s);
-      case 512: return norm_v_go<bf16_t, 64, 1>(a, s);
+      case 512: return norm_v_go<bf16_t, 32, 2>(a, s);
       case 1024: return norm_v_go<bf16_t, 64, 2>(a, s);
     }
   } else {
