@@ -6,11 +6,13 @@ One step = one whole decode, wanvae_decode through the C ABI, of seeded syntheti
 accumulation) -> video [1, 3, 121, 704, 1280]. The latents and the fp32 weights are resident
 in HBM before the timed region; the decode's own weight rounding/repacking is inside it.
 
-Prints one JSON line: decoded frames/s, the dominant kernel's roofline (the conv kernels,
-all launches of the timed decodes: algorithmic FLOPs / HIP-event kernel time, against the
-bf16 dense MFMA peak; the HBM bytes per launch from the stored counter measurement while the
-kernel source it was taken on is unchanged), the other kernel classes, and the CPU oracle
-timed on a bounded sample.
+Prints one JSON line: decoded frames/s over the timed decodes (by default the library's
+two-stream chunk pipeline), the dominant kernel's roofline (the conv kernels, all launches of
+K more decodes run in chunk order on one stream so that each kernel's HIP-event time is its
+own: algorithmic FLOPs / event time, against the bf16 dense MFMA peak; the HBM bytes per
+launch from the stored counter measurement while the kernel source it was taken on is
+unchanged), the other kernel classes from the same decodes, and the CPU oracle timed on a
+bounded sample.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--workload NAME]
     python bench.py --copy-bytes N    # three device-to-device copies of N bytes (counter scale)
@@ -178,6 +180,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0)
     ap.add_argument("--workload", default="ti2v5b_landscape_bf16", choices=sorted(DECODES) + sorted(SINGLE))
+    ap.add_argument("--no-pipeline", action="store_true",
+                    help="decode in chunk order on one stream (default: the two-stream chunk pipeline)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the decoder here runs on a single MI355X (got --gpus {args.gpus}); "
@@ -196,6 +200,7 @@ def main():
     from video_vae_decoding_amd import wanvae
 
     dev = torch.device("cuda:0")
+    wanvae.wanvae_set_decode_pipeline(not args.no_pipeline)
     cfg_name, mode = DECODES[args.workload]
     cfg = synthetic.DECODE_CONFIGS[cfg_name]
     log("generating inputs ...")
@@ -211,18 +216,32 @@ def main():
         wanvae.wanvae_decode(zt, Wt, dtype, video=video, workspace=ws)
         torch.cuda.synchronize()
         log(f"warmup {i + 1}/{args.warmup} done")
-    wanvae.wanvae_profile_enable(True)
+    # the timed region: K decodes as a caller runs them (the two-stream chunk pipeline unless
+    # --no-pipeline)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         wanvae.wanvae_decode(zt, Wt, dtype, video=video, workspace=ws)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    prof = {k: wanvae.wanvae_profile_read(getattr(wanvae, "K" + k.upper())) for k in ("conv", "norm", "attn", "other")}
-    wanvae.wanvae_profile_enable(False)
     elapsed = t1 - t0
     log(f"timed {args.steps} decodes in {elapsed:.3f} s")
     assert torch.isfinite(video).all()
+    # the kernel region: K more decodes in chunk order on one stream, every kernel timed with HIP
+    # events on its stream. Run alone, each kernel's event time is its own: with the pipeline
+    # the two streams' kernels share the chip and their event times overlap.
+    wanvae.wanvae_set_decode_pipeline(False)
+    wanvae.wanvae_profile_enable(True)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for i in range(args.steps):
+        wanvae.wanvae_decode(zt, Wt, dtype, video=video, workspace=ws)
+    torch.cuda.synchronize()
+    t3 = time.perf_counter()
+    prof = {k: wanvae.wanvae_profile_read(getattr(wanvae, "K" + k.upper())) for k in ("conv", "norm", "attn", "other")}
+    wanvae.wanvae_profile_enable(False)
+    wanvae.wanvae_set_decode_pipeline(not args.no_pipeline)
+    log(f"kernel region: {args.steps} decodes in chunk order in {t3 - t2:.3f} s")
 
     conv = prof["conv"]
     conv_tflops = conv["flops"] / (conv["ms"] * 1e-3) / 1e12
@@ -247,7 +266,7 @@ def main():
         "config": {"workload": f"ti2v5b_vae_decode_{16 * cfg.h}x{16 * cfg.w}x{cfg.frames}_{mode}" + ("" if cfg.B == 1 else f"_b{cfg.B}"),
                    "latent": [cfg.B, 48, cfg.T, cfg.h, cfg.w],
                    "video": [cfg.B, 3, cfg.frames, 16 * cfg.h, 16 * cfg.w], "weights": f"random-init, seed {cfg.seed}",
-                   "accumulate": "fp32"},
+                   "accumulate": "fp32", "pipeline": not args.no_pipeline},
         "roofline": {"bound": "mfma",
                      "kernel": ("conv (k_conv_halo for the 3x3 convs, k_conv_dma for the rest; all launches of a decode)"
                                 if mode == "bf16" else "conv (k_conv, fp32 MFMA; all launches of a decode)"),
@@ -256,6 +275,10 @@ def main():
                      "launches": conv["launches"], "avg_launch_ms": round(conv["ms"] / max(1, conv["launches"]), 4),
                      "algorithmic_tflop_per_step": round(conv["flops"] / args.steps / 1e12, 2)},
         "kernels": kernels,
+        "chunk_order": {"frames/s": round(frames * args.steps / (t3 - t2), 3),
+                        "ms_per_step": round((t3 - t2) / args.steps * 1e3, 2),
+                        "note": "the kernel region: the same decodes in chunk order on one stream, "
+                                "with per-kernel HIP events (roofline and kernels come from it)"},
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on its sample ...")

@@ -170,6 +170,22 @@ int wanvae_profile_read(int kind, double *ms, int64_t *launches, double *flops, 
 #define WANVAE_CONV_KERNELS 13
 int wanvae_set_conv_kernel(int kernel);
 
+/*
+ * Decode pipeline switch. With on = 1 (the default) wanvae_decode runs each latent frame's
+ * work as two stages on two streams of its own (made once per device, default priority):
+ * conv_in, the mid block and up block 0 of frame i+1 overlap up blocks 1-3 and conv_out of
+ * frame i. This is the wavefront over the causal chunk loop that the page's chunked form
+ * allows: a stage depends only on its own earlier chunks and on the stage before it of the
+ * same chunk. Events order the stages; `stream` waits for both before the call's last
+ * enqueued work, so the call stays ordered on `stream` as documented above. Every kernel
+ * receives the same arguments either way, so the video is bit-identical with on = 0, which
+ * runs everything on `stream` in chunk order. Decodes of one latent frame always run on
+ * `stream`. Concurrent decodes on one device share the two streams and run one after the
+ * other. Returns WANVAE_EARG for any value but 0 or 1. Do not change it while another thread
+ * is enqueueing work.
+ */
+int wanvae_set_decode_pipeline(int on);
+
 /* Message for the last failed call on this thread ("" if none). Valid until the next call. */
 const char *wanvae_last_error(void);
 

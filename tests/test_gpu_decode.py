@@ -132,6 +132,63 @@ def test_tiny_decode_causal_prefix_batch_independence_determinism(tiny):
     assert np.array_equal(to_np(gpu_decode(z3[1:].copy(), W, "bf16")), full[1:])
 
 
+@pytest.fixture
+def pipeline():
+    """Sets the decode pipeline switch for one test and restores the default afterwards."""
+    try:
+        yield wanvae.wanvae_set_decode_pipeline
+    finally:
+        wanvae.wanvae_set_decode_pipeline(True)
+
+
+@pytest.mark.parametrize("mode", ["fp32", "bf16"])
+def test_decode_pipeline_matches_chunk_order_bit_for_bit(pipeline, mode):
+    """B = 2, T = 7, 3x5 latent: seven chunks, so the two-stream pipeline reuses each of
+    level 1's two input buffers three times (the wait on the second stage of chunk i-2) and
+    runs the split-K level-0 convs of one chunk beside the levels above of the one before.
+    The video must equal the decode in chunk order on one stream bit for bit, and match the
+    oracle: fp32 to 5e-4; bf16 with PSNR >= 40 dB and within the bf16 decode's own distance
+    from the fp32 decode (the oracle's, on these inputs: mean 1x, max 1.5x). Over seven
+    chunks the tiny bf16 decoder carries any early rounding difference into every later
+    frame; its distance from the fp32 decode is the scale such differences settle at. The
+    oracle's float32-sum variant stays closer than that on these latents for its first frames
+    only by chance (mean 0.0002 at frame 0 against 0.0025 on the T = 4 inputs above)."""
+    z = synthetic.normal(8, "latents_pipe", (2, 48, 7, 3, 5))
+    W = synthetic.gen_weights(16, 8, 0.1)
+    say("tiny B2 T7 pipeline on / off", mode)
+    pipeline(True)
+    on = to_np(gpu_decode(z, W, mode))
+    pipeline(False)
+    off = to_np(gpu_decode(z, W, mode))
+    assert np.array_equal(on, off)
+    want = oracle.decode(z, W, mode)
+    if mode == "fp32":
+        gate(on, want, mode, "tiny B2 T7 fp32")
+        return
+    scale = np.abs(want - oracle.decode(z, W, "fp32").astype(np.float64))
+    d = np.abs(on.astype(np.float64) - want)
+    p = oracle.psnr(on, want)
+    say("tiny B2 T7 bf16 max", d.max(), "mean", d.mean(), "psnr", p, "bf16-fp32 max", scale.max(), "mean", scale.mean())
+    assert p >= 40, p
+    assert d.mean() <= scale.mean(), (d.mean(), scale.mean())
+    assert d.max() <= 1.5 * scale.max(), (d.max(), scale.max())
+
+
+def test_small32_decode_pipeline_matches_chunk_order_bit_for_bit(pipeline):
+    """decoder_base_dim 32, T = 5, 8x12 latent: the halo-tile kernels and the level-0 split K
+    on both streams; on and off agree bit for bit."""
+    cfg = synthetic.DECODE_CONFIGS["small32"]
+    z = synthetic.normal(9, "latents_pipe32", (1, 48, 5, cfg.h, cfg.w))
+    W = cfg.weights()
+    say("small32 T5 pipeline on / off")
+    pipeline(True)
+    on = gpu_decode(z, W, "bf16")
+    pipeline(False)
+    off = gpu_decode(z, W, "bf16")
+    assert torch.equal(on, off)
+    assert torch.isfinite(on).all()
+
+
 def test_unpatchify_channel_map_and_clamp_are_exact(tiny):
     """conv_out weights zero, biases c: every pixel of colour k at row offset i and column
     offset j equals clamp(bias[4k + 2j + i]), bit for bit."""
@@ -208,5 +265,16 @@ def test_full_decode_first_frames_match_oracle_samples(config, mode):
     prefix = gpu_decode(np.ascontiguousarray(z[:, :, :2]), W, mode)
     assert torch.equal(prefix, video[:, :, :5])
     assert torch.isfinite(video).all()
-    del video, prefix
+    del prefix
+    if (config, mode) == ("ti2v5b_landscape", "bf16"):
+        # the two-stream pipeline (the default) against the decode in chunk order, bit for bit
+        say("full decode in chunk order on one stream")
+        wanvae.wanvae_set_decode_pipeline(False)
+        try:
+            ordered = gpu_decode(z, W, mode)
+        finally:
+            wanvae.wanvae_set_decode_pipeline(True)
+        assert torch.equal(ordered, video)
+        del ordered
+    del video
     torch.cuda.empty_cache()

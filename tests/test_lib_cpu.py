@@ -173,3 +173,15 @@ def test_conv_kernel_selection_range():
                 W.wanvae_set_conv_kernel(bad)
     finally:
         W.wanvae_set_conv_kernel(-1)
+
+
+def test_decode_pipeline_switch():
+    L = W.lib()
+    try:
+        assert L.wanvae_set_decode_pipeline(0) == W.OK
+        assert L.wanvae_set_decode_pipeline(1) == W.OK
+        for bad in (-1, 2):
+            assert L.wanvae_set_decode_pipeline(bad) == W.EARG
+            assert "0 or 1" in L.wanvae_last_error().decode()
+    finally:
+        W.wanvae_set_decode_pipeline(True)

@@ -19,6 +19,9 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
+#include <memory>
+#include <mutex>
 #include <string>
 #include <unordered_map>
 #include <vector>
@@ -572,6 +575,34 @@ struct Level {
   void* tb = nullptr;  // time conv output (2F frames), up blocks 0 and 1
 };
 
+// Streams and events of the two-stage chunk pipeline of the decoder: one set per device,
+// made on first use and kept until the process ends. Both streams have the default priority
+// and do not synchronise with the null stream; the events carry no timing.
+struct Pipe {
+  std::mutex mu;  // held while one decode enqueues its work on these streams
+  hipStream_t s[2] = {};
+  hipEvent_t start = nullptr, end[2] = {}, a[2] = {}, b[2] = {};
+};
+static std::atomic<int> g_pipeline{1};
+
+static int pipe_for_device(Pipe** out) {
+  static std::mutex mu;
+  static std::map<int, std::unique_ptr<Pipe>> pipes;
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lk(mu);
+  std::unique_ptr<Pipe>& slot = pipes[dev];
+  if (!slot) {
+    std::unique_ptr<Pipe> p(new Pipe);
+    for (int k = 0; k < 2; ++k) HIP_TRY(hipStreamCreateWithFlags(&p->s[k], hipStreamNonBlocking));
+    hipEvent_t* ev[7] = {&p->start, &p->end[0], &p->end[1], &p->a[0], &p->a[1], &p->b[0], &p->b[1]};
+    for (hipEvent_t* e : ev) HIP_TRY(hipEventCreateWithFlags(e, hipEventDisableTiming));
+    slot = std::move(p);
+  }
+  *out = slot.get();
+  return WANVAE_OK;
+}
+
 class Decoder {
  public:
   Decoder(const WeightMap& m, const Topology& tp, int dtype, int B, int T, int h, int w)
@@ -590,6 +621,7 @@ class Decoder {
     for (auto& g : tp_.norms)
       if (int rc = prep_vec(ar, dt_, m_.at(g.first), g.second, gam_[g.first], st)) return rc;
     const int c4 = tp_.c4, c2 = tp_.c2, c1 = tp_.c1;
+    up_specs(tp_.base, u_);
     const int fmax[4] = {1, T_ > 1 ? 2 : 1, T_ > 1 ? 4 : 1, T_ > 1 ? 4 : 1};
     const int cmax[4] = {c4, c4, c4, c2};
     for (int l = 0; l < 4; ++l) {
@@ -618,8 +650,7 @@ class Decoder {
     };
     resnet_rings("decoder.mid_block.resnets.0", 0, c4, c4);
     resnet_rings("decoder.mid_block.resnets.1", 0, c4, c4);
-    UpSpec u[4];
-    up_specs(tp_.base, u);
+    const UpSpec* u = u_;
     for (int i = 0; i < 4; ++i) {
       const std::string p = "decoder.up_blocks." + std::to_string(i);
       for (int j = 0; j < 3; ++j) resnet_rings(p + ".resnets." + std::to_string(j), i, j == 0 ? u[i].cin : u[i].cout, u[i].cout);
@@ -627,27 +658,55 @@ class Decoder {
     }
     ring("decoder.conv_out", 3, c1);
     plan_attn_bufs(ar, ab_, B_, h_ * w_, c4, dt_, false);
+    // level 1's input frames, second buffer (odd chunks)
+    x1b_ = ar.take((size_t)lv_[1].F * B_ * lv_[1].H * lv_[1].W * lv_[1].C * es_);
     // split-K scratch for the level-0 convs (one frame of B x h x w positions; at most 3 c4
-    // output channels, the attention's q-k-v conv)
-    split_ = take_split(ar, (int64_t)B_ * h_ * w_, 3 * (int64_t)c4);
+    // output channels, the attention's q-k-v conv), one per stage so that the two stages can
+    // run at once with the same split of every conv
+    splitA_ = take_split(ar, (int64_t)B_ * h_ * w_, 3 * (int64_t)c4);
+    splitB_ = take_split(ar, (int64_t)B_ * h_ * w_, 3 * (int64_t)c4);
     return WANVAE_OK;
   }
 
-  int run(const void* z, int z_dtype, void* video) {
-    SplitScope scope(split_);
-    const int64_t zf = (int64_t)B_ * h_ * w_ * tp_.z;
-    HIP_TRY(launch_ncthw_to_frames(z, z_dtype, zt_, dt_, B_, tp_.z, tp_.z, T_, h_, w_, st_));
-    {  // post_quant_conv over all T latent frames at once (frames folded into the batch)
+  // Enqueues the decode. With `pipe`, chunk i's first stage (conv_in, the mid block and up
+  // block 0, on pipe->s[0]) runs while chunk i-1's second stage (up blocks 1-3 and conv_out,
+  // on pipe->s[1]) is still running; every kernel gets the arguments it gets without `pipe`.
+  int run(const void* z, int z_dtype, void* video, Pipe* pipe) {
+    {
+      SplitScope scope(splitA_);
+      HIP_TRY(launch_ncthw_to_frames(z, z_dtype, zt_, dt_, B_, tp_.z, tp_.z, T_, h_, w_, st_));
+      // post_quant_conv over all T latent frames at once (frames folded into the batch)
       ConvCall cc;
       cc.a.mode = kEpiFrames;
       set_out(cc.a, frames_of(pq_, 1, 0, (int64_t)h_ * w_ * tp_.z, es_), tp_.z);
       const FrameRef in = frames_of(zt_, 1, 0, (int64_t)h_ * w_ * tp_.z, es_);
       if (int rc = run_conv(cw_.at("post_quant_conv"), in, T_ * B_, h_, w_, h_, w_, 1, false, cc, dt_, st_)) return rc;
     }
-    for (int i = 0; i < T_; ++i)
-      if (int rc = chunk(i, video)) return rc;
-    (void)zf;
-    return WANVAE_OK;
+    if (!pipe) {
+      for (int i = 0; i < T_; ++i) {
+        {
+          SplitScope scope(splitA_);
+          if (int rc = chunk_a(i)) return rc;
+        }
+        SplitScope scope(splitB_);
+        if (int rc = chunk_b(i, video)) return rc;
+      }
+      return WANVAE_OK;
+    }
+    const hipStream_t caller = st_;
+    HIP_TRY(hipEventRecord(pipe->start, caller));
+    for (int k = 0; k < 2; ++k) HIP_TRY(hipStreamWaitEvent(pipe->s[k], pipe->start, 0));
+    int rc = WANVAE_OK;
+    for (int i = 0; i < T_ && rc == WANVAE_OK; ++i) rc = pipelined_chunk(i, video, *pipe);
+    st_ = caller;
+    // the caller's stream waits for both stages, also after an error (the workspace may be
+    // released on it next)
+    for (int k = 0; k < 2; ++k) {
+      hipError_t e = hipEventRecord(pipe->end[k], pipe->s[k]);
+      if (e == hipSuccess) e = hipStreamWaitEvent(caller, pipe->end[k], 0);
+      if (e != hipSuccess && rc == WANVAE_OK) rc = fail(WANVAE_EHIP, "joining the decode streams: %s", hipGetErrorString(e));
+    }
+    return rc;
   }
 
  private:
@@ -688,8 +747,41 @@ class Decoder {
     return WANVAE_OK;
   }
 
-  int chunk(int i, void* video) {
-    const bool first = i == 0;
+  // Chunk i on the two pipeline streams. Level 1's input is double-buffered by chunk parity:
+  // chunk i's first stage writes the buffer chunk i-2's second stage read, so it waits for
+  // that stage; the second stage waits for its own chunk's first stage.
+  int pipelined_chunk(int i, void* video, Pipe& pp) {
+    const int par = i & 1;
+    if (i >= 2) HIP_TRY(hipStreamWaitEvent(pp.s[0], pp.b[par], 0));
+    st_ = pp.s[0];
+    {
+      SplitScope scope(splitA_);
+      if (int rc = chunk_a(i)) return rc;
+    }
+    HIP_TRY(hipEventRecord(pp.a[par], pp.s[0]));
+    HIP_TRY(hipStreamWaitEvent(pp.s[1], pp.a[par], 0));
+    st_ = pp.s[1];
+    {
+      SplitScope scope(splitB_);
+      if (int rc = chunk_b(i, video)) return rc;
+    }
+    HIP_TRY(hipEventRecord(pp.b[par], pp.s[1]));
+    return WANVAE_OK;
+  }
+
+  // Input frames of up block b for chunk i (level 1: one buffer per chunk parity).
+  void* block_in(int b, int i) const { return b == 1 && (i & 1) ? x1b_ : lv_[b].x[0]; }
+
+  // Frames per chunk at level l: one for the first chunk (no time conv runs on it), else
+  // doubled by each temporal up block below l.
+  int frames_at(int l, int i) const {
+    int F = 1;
+    for (int b = 0; b < l && i > 0; ++b) F *= u_[b].temporal ? 2 : 1;
+    return F;
+  }
+
+  // First stage of chunk i: conv_in, the mid block and up block 0.
+  int chunk_a(int i) {
     const int c4 = tp_.c4;
     // conv_in: latent frames i-2, i-1 (history) and i, read in place from the post_quant output
     {
@@ -709,70 +801,78 @@ class Decoder {
         return rc;
     }
     if (int rc = resnet("decoder.mid_block.resnets.1", 0, 1, x2, c4, c4, x0)) return rc;
+    return up_block(0, i, nullptr);
+  }
 
-    UpSpec u[4];
-    up_specs(tp_.base, u);
-    int F = 1;
-    for (int b = 0; b < 4; ++b) {
-      Level& L = lv_[b];
-      const std::string p = "decoder.up_blocks." + std::to_string(b);
-      const FrameRef xin = lvl_frames(b, L.x[0], F, u[b].cin);
-      const FrameRef xa = lvl_frames(b, L.x[1], F, u[b].cout), xb = lvl_frames(b, L.x[2], F, u[b].cout);
-      if (int rc = resnet(p + ".resnets.0", b, F, xin, u[b].cin, u[b].cout, xa)) return rc;
-      if (int rc = resnet(p + ".resnets.1", b, F, xa, u[b].cout, u[b].cout, xb)) return rc;
-      const bool tconv = u[b].temporal && !first;
-      Ring* tr = tconv ? &rings_.at(p + ".upsampler.time_conv") : nullptr;
-      const FrameRef r2out = tconv ? tr->write(F) : xa;
-      if (int rc = resnet(p + ".resnets.2", b, F, xb, u[b].cout, u[b].cout, r2out)) return rc;
-      if (!u[b].spatial) {
-        // norm_out + SiLU -> conv_out -> unpatchify + clamp straight into the video
-        Ring& ro = rings_.at("decoder.conv_out");
-        if (int rc = run_norm(r2out, ro.write(F), F, B_, L.H * L.W, u[b].cout, gam_.at("decoder.norm_out.gamma"), true,
-                              dt_, st_))
-          return rc;
-        const ConvW& cw = cw_.at("decoder.conv_out");
-        ConvCall cc;
-        cc.a.mode = kEpiVideo;
-        cc.a.video = video;
-        cc.a.vF = 4 * T_ - 3;
-        cc.a.vf0 = first ? 0 : 4 * i - 3;
-        if (int rc = run_conv(cw, ro.read(F), B_, L.H, L.W, L.H, L.W, F, false, cc, dt_, st_)) return rc;
-        ro.commit(F);
-        break;
-      }
-      FrameRef src = r2out;
-      int Fs = F;
-      if (tconv) {
-        // upsample3d's time conv: C -> 2C, channel c -> frame 2t, channel C + c -> frame 2t + 1
-        const ConvW& cw = cw_.at(p + ".upsampler.time_conv");
-        ConvCall cc;
-        cc.a.mode = kEpiInterleave;
-        src = lvl_frames(b, L.tb, 2 * F, u[b].cout);
-        set_out(cc.a, src, u[b].cout);
-        if (int rc = run_conv(cw, tr->read(F), B_, L.H, L.W, L.H, L.W, F, false, cc, dt_, st_)) return rc;
-        tr->commit(F);
-        Fs = 2 * F;
-      }
-      // upsample2d (nearest x2 read through the conv's addressing, 3x3 conv) + DupUp3D(block input)
-      Level& N = lv_[b + 1];
-      const ConvW& cw = cw_.at(p + ".upsampler.resample.1");
-      ConvCall cc;
-      cc.a.mode = kEpiFrames;
-      set_out(cc.a, lvl_frames(b + 1, N.x[0], Fs, u[b].cout), u[b].cout);
-      const int ft = u[b].temporal ? 2 : 1;
-      cc.a.has_dup = 1;
-      for (int t = 0; t < F; ++t) {
-        cc.a.dup[t] = xin.f[t];
-        cc.a.dup_bs[t] = xin.bs[t];
-      }
-      cc.a.dup_C = u[b].cin;
-      cc.a.dup_ft = ft;
-      cc.a.dup_r = u[b].cout * ft * 4 / u[b].cin;
-      cc.a.dup_shift = first ? ft - 1 : 0;
-      if (int rc = run_conv(cw, src, B_, L.H, L.W, N.H, N.W, Fs, true, cc, dt_, st_)) return rc;
-      F = Fs;
-    }
+  // Second stage of chunk i: up blocks 1-3, norm_out, conv_out.
+  int chunk_b(int i, void* video) {
+    for (int b = 1; b < 4; ++b)
+      if (int rc = up_block(b, i, video)) return rc;
     return WANVAE_OK;
+  }
+
+  // Up block b of chunk i: three residual blocks, then the upsampler into level b+1, or (the
+  // last block) norm_out + SiLU and conv_out into the video.
+  int up_block(int b, int i, void* video) {
+    const bool first = i == 0;
+    const UpSpec* u = u_;
+    const int F = frames_at(b, i);
+    Level& L = lv_[b];
+    const std::string p = "decoder.up_blocks." + std::to_string(b);
+    const FrameRef xin = lvl_frames(b, block_in(b, i), F, u[b].cin);
+    const FrameRef xa = lvl_frames(b, L.x[1], F, u[b].cout), xb = lvl_frames(b, L.x[2], F, u[b].cout);
+    if (int rc = resnet(p + ".resnets.0", b, F, xin, u[b].cin, u[b].cout, xa)) return rc;
+    if (int rc = resnet(p + ".resnets.1", b, F, xa, u[b].cout, u[b].cout, xb)) return rc;
+    const bool tconv = u[b].temporal && !first;
+    Ring* tr = tconv ? &rings_.at(p + ".upsampler.time_conv") : nullptr;
+    const FrameRef r2out = tconv ? tr->write(F) : xa;
+    if (int rc = resnet(p + ".resnets.2", b, F, xb, u[b].cout, u[b].cout, r2out)) return rc;
+    if (!u[b].spatial) {
+      // norm_out + SiLU -> conv_out -> unpatchify + clamp straight into the video
+      Ring& ro = rings_.at("decoder.conv_out");
+      if (int rc = run_norm(r2out, ro.write(F), F, B_, L.H * L.W, u[b].cout, gam_.at("decoder.norm_out.gamma"), true,
+                            dt_, st_))
+        return rc;
+      const ConvW& cw = cw_.at("decoder.conv_out");
+      ConvCall cc;
+      cc.a.mode = kEpiVideo;
+      cc.a.video = video;
+      cc.a.vF = 4 * T_ - 3;
+      cc.a.vf0 = first ? 0 : 4 * i - 3;
+      if (int rc = run_conv(cw, ro.read(F), B_, L.H, L.W, L.H, L.W, F, false, cc, dt_, st_)) return rc;
+      ro.commit(F);
+      return WANVAE_OK;
+    }
+    FrameRef src = r2out;
+    int Fs = F;
+    if (tconv) {
+      // upsample3d's time conv: C -> 2C, channel c -> frame 2t, channel C + c -> frame 2t + 1
+      const ConvW& cw = cw_.at(p + ".upsampler.time_conv");
+      ConvCall cc;
+      cc.a.mode = kEpiInterleave;
+      src = lvl_frames(b, L.tb, 2 * F, u[b].cout);
+      set_out(cc.a, src, u[b].cout);
+      if (int rc = run_conv(cw, tr->read(F), B_, L.H, L.W, L.H, L.W, F, false, cc, dt_, st_)) return rc;
+      tr->commit(F);
+      Fs = 2 * F;
+    }
+    // upsample2d (nearest x2 read through the conv's addressing, 3x3 conv) + DupUp3D(block input)
+    Level& N = lv_[b + 1];
+    const ConvW& cw = cw_.at(p + ".upsampler.resample.1");
+    ConvCall cc;
+    cc.a.mode = kEpiFrames;
+    set_out(cc.a, lvl_frames(b + 1, block_in(b + 1, i), Fs, u[b].cout), u[b].cout);
+    const int ft = u[b].temporal ? 2 : 1;
+    cc.a.has_dup = 1;
+    for (int t = 0; t < F; ++t) {
+      cc.a.dup[t] = xin.f[t];
+      cc.a.dup_bs[t] = xin.bs[t];
+    }
+    cc.a.dup_C = u[b].cin;
+    cc.a.dup_ft = ft;
+    cc.a.dup_r = u[b].cout * ft * 4 / u[b].cin;
+    cc.a.dup_shift = first ? ft - 1 : 0;
+    return run_conv(cw, src, B_, L.H, L.W, N.H, N.W, Fs, true, cc, dt_, st_);
   }
 
   const WeightMap& m_;
@@ -788,7 +888,9 @@ class Decoder {
   void* zt_ = nullptr;
   void* pq_ = nullptr;
   AttnBufs ab_;
-  SplitBuf split_;
+  UpSpec u_[4];
+  void* x1b_ = nullptr;
+  SplitBuf splitA_, splitB_;
 };
 
 static int check_dtype(int dtype, const char* what) {
@@ -852,6 +954,12 @@ int wanvae_set_conv_kernel(int kernel) {
   return WANVAE_OK;
 }
 
+int wanvae_set_decode_pipeline(int on) {
+  if (on != 0 && on != 1) return fail(WANVAE_EARG, "decode pipeline switch %d is not 0 or 1", on);
+  g_pipeline.store(on);
+  return WANVAE_OK;
+}
+
 int wanvae_version(void) { return 100; }
 
 int wanvae_decode_workspace_size(int64_t B, int64_t T, int64_t h, int64_t w, const wanvae_tensor* weights,
@@ -889,7 +997,13 @@ int wanvae_decode(const void* z, int32_t z_dtype, int64_t B, int64_t T, int64_t 
   Arena ar;
   ar.base = (char*)ws;
   int rc = d.plan(ar, st);
-  if (rc == WANVAE_OK) rc = d.run(z, z_dtype, video);
+  Pipe* pipe = nullptr;
+  if (rc == WANVAE_OK && T > 1 && g_pipeline.load(std::memory_order_relaxed)) rc = pipe_for_device(&pipe);
+  if (rc == WANVAE_OK) {
+    std::unique_lock<std::mutex> lk;
+    if (pipe) lk = std::unique_lock<std::mutex>(pipe->mu);
+    rc = d.run(z, z_dtype, video, pipe);
+  }
   if (!workspace) {
     hipError_t e = hipFreeAsync(ws, st);
     if (rc == WANVAE_OK && e != hipSuccess) rc = fail(WANVAE_EHIP, "hipFreeAsync: %s", hipGetErrorString(e));

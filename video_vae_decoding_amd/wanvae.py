@@ -63,9 +63,11 @@ def lib() -> ctypes.CDLL:
         L.wanvae_last_error.argtypes = []
         L.wanvae_version.argtypes = []
         L.wanvae_set_conv_kernel.argtypes = [ctypes.c_int]
+        L.wanvae_set_decode_pipeline.argtypes = [ctypes.c_int]
         for f in ("wanvae_decode_workspace_size", "wanvae_decode", "wanvae_causal_conv3d_workspace_size",
                   "wanvae_causal_conv3d", "wanvae_attn_block_workspace_size", "wanvae_attn_block", "wanvae_version",
-                  "wanvae_profile_enable", "wanvae_profile_read", "wanvae_set_conv_kernel"):
+                  "wanvae_profile_enable", "wanvae_profile_read", "wanvae_set_conv_kernel",
+                  "wanvae_set_decode_pipeline"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -216,6 +218,13 @@ CONV_KERNELS = 13
 def wanvae_set_conv_kernel(kernel: int) -> None:
     """Use conv kernel ``kernel`` wherever it can run a conv (-1: each conv's default)."""
     check(lib().wanvae_set_conv_kernel(kernel))
+
+
+def wanvae_set_decode_pipeline(on: bool) -> None:
+    """Overlap each latent frame's low-level stage with the previous frame's high levels
+    on two streams (True, the default) or run the decode in chunk order on the caller's
+    stream (False). The video is bit-identical either way."""
+    check(lib().wanvae_set_decode_pipeline(1 if on else 0))
 
 
 def wanvae_profile_enable(on: bool = True) -> None:
