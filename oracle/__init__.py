@@ -22,9 +22,13 @@ Sums inside a convolution, matmul or softmax are accumulated in float64 unless
 ``acc="f32"`` is passed (allowed for the full-size configurations, where the
 page itself says the bf16 and fp32 kernels accumulate in float32).
 
+``tiled.py`` holds the spatially tiled decode of the diffusers PR page on Wan
+tiling, with the blend rule read as its module docstring says.
+
 Every function here is pinned by a ``-m "not gpu"`` test in
-``tests/test_oracle_ops.py`` or ``tests/test_oracle_decoder.py`` against brute
-force, a library routine, a closed form or an invariant the page states.
+``tests/test_oracle_ops.py``, ``tests/test_oracle_decoder.py`` or
+``tests/test_oracle_tiled.py`` against brute force, a library routine, a closed
+form or an invariant the pages state.
 """
 from .decoder import (  # noqa: F401
     MODES,
@@ -46,3 +50,4 @@ from .decoder import (  # noqa: F401
     time_upsample,
     unpatchify,
 )
+from .tiled import compose, decode_tiled, tile_grid  # noqa: F401
