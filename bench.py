@@ -19,6 +19,7 @@ bounded sample.
 
 --workload picks another of the measured configurations (default ti2v5b_landscape_bf16):
 ti2v5b_landscape_fp32, ti2v5b_portrait_bf16, ti2v5b_landscape_b2_bf16 (whole decodes, frames/s),
+ti2v5b_landscape_bf16_tiled (the spatially tiled decode, tile 256 / stride 192 video pixels),
 conv1024_l0_bf16, conv256_l3_bf16 (one causal conv, TFLOP/s), attn1024_31f_bf16 (the attention
 block over 31 frames, TFLOP/s), attn384_s14400_21f_bf16 and attn1024_s14400_21f_bf16 (the block
 over 21 frames of the Wan2.1 720p latent, 90x160 positions, at widths 384 and 1024).
@@ -93,7 +94,9 @@ def copy_calibration(nbytes):
 
 
 DECODES = {"ti2v5b_landscape_bf16": ("ti2v5b_landscape", "bf16"), "ti2v5b_landscape_fp32": ("ti2v5b_landscape", "fp32"),
-           "ti2v5b_portrait_bf16": ("ti2v5b_portrait", "bf16"), "ti2v5b_landscape_b2_bf16": ("ti2v5b_landscape_b2", "bf16")}
+           "ti2v5b_portrait_bf16": ("ti2v5b_portrait", "bf16"), "ti2v5b_landscape_b2_bf16": ("ti2v5b_landscape_b2", "bf16"),
+           "ti2v5b_landscape_bf16_tiled": ("ti2v5b_landscape", "bf16")}
+TILED = {"ti2v5b_landscape_bf16_tiled": ((256, 256), (192, 192))}  # the page's default tile and stride
 SINGLE = {"conv1024_l0_bf16": ("conv", "conv1024_l0"), "conv256_l3_bf16": ("conv", "conv256_l3"),
           "attn1024_31f_bf16": ("attn", "attn1024_31f"), "attn384_s14400_21f_bf16": ("attn", "attn384_s14400_21f"),
           "attn1024_s14400_21f_bf16": ("attn", "attn1024_s14400_21f")}
@@ -211,9 +214,17 @@ def main():
     peak = PEAK_BF16_TFLOPS if mode == "bf16" else PEAK_FP32_TFLOPS
     frames = cfg.B * cfg.frames
     video = torch.empty((cfg.B, 3, cfg.frames, 16 * cfg.h, 16 * cfg.w), dtype=dtype, device=dev)
-    ws = torch.empty(wanvae.decode_workspace_size(cfg.B, cfg.T, cfg.h, cfg.w, Wt, dtype), dtype=torch.uint8, device=dev)
+    tiled = TILED.get(args.workload)
+    if tiled:
+        ws = torch.empty(wanvae.decode_tiled_workspace_size(cfg.B, cfg.T, cfg.h, cfg.w, Wt, dtype, *tiled),
+                         dtype=torch.uint8, device=dev)
+        run = lambda: wanvae.wanvae_decode_tiled(zt, Wt, dtype, *tiled, video=video, workspace=ws)
+    else:
+        ws = torch.empty(wanvae.decode_workspace_size(cfg.B, cfg.T, cfg.h, cfg.w, Wt, dtype), dtype=torch.uint8,
+                         device=dev)
+        run = lambda: wanvae.wanvae_decode(zt, Wt, dtype, video=video, workspace=ws)
     for i in range(args.warmup):
-        wanvae.wanvae_decode(zt, Wt, dtype, video=video, workspace=ws)
+        run()
         torch.cuda.synchronize()
         log(f"warmup {i + 1}/{args.warmup} done")
     # the timed region: K decodes as a caller runs them (the two-stream chunk pipeline unless
@@ -221,7 +232,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        wanvae.wanvae_decode(zt, Wt, dtype, video=video, workspace=ws)
+        run()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     elapsed = t1 - t0
@@ -235,7 +246,7 @@ def main():
     torch.cuda.synchronize()
     t2 = time.perf_counter()
     for i in range(args.steps):
-        wanvae.wanvae_decode(zt, Wt, dtype, video=video, workspace=ws)
+        run()
     torch.cuda.synchronize()
     t3 = time.perf_counter()
     prof = {k: wanvae.wanvae_profile_read(getattr(wanvae, "K" + k.upper())) for k in ("conv", "norm", "attn", "other")}
@@ -263,10 +274,11 @@ def main():
         "vs_baseline": None,
         "dtype": mode,
         "data": "synthetic",
-        "config": {"workload": f"ti2v5b_vae_decode_{16 * cfg.h}x{16 * cfg.w}x{cfg.frames}_{mode}" + ("" if cfg.B == 1 else f"_b{cfg.B}"),
+        "config": {"workload": f"ti2v5b_vae_decode_{16 * cfg.h}x{16 * cfg.w}x{cfg.frames}_{mode}" + ("" if cfg.B == 1 else f"_b{cfg.B}")
+                   + ("" if not tiled else f"_tiled{tiled[0][0]}s{tiled[1][0]}"),
                    "latent": [cfg.B, 48, cfg.T, cfg.h, cfg.w],
                    "video": [cfg.B, 3, cfg.frames, 16 * cfg.h, 16 * cfg.w], "weights": f"random-init, seed {cfg.seed}",
-                   "accumulate": "fp32", "pipeline": not args.no_pipeline},
+                   "accumulate": "fp32", "pipeline": not args.no_pipeline, "workspace_bytes": ws.numel()},
         "roofline": {"bound": "mfma",
                      "kernel": ("conv (k_conv_halo for the 3x3 convs, k_conv_dma for the rest; all launches of a decode)"
                                 if mode == "bf16" else "conv (k_conv, fp32 MFMA; all launches of a decode)"),

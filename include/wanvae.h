@@ -171,6 +171,39 @@ int wanvae_profile_read(int kind, double *ms, int64_t *launches, double *flops, 
 int wanvae_set_conv_kernel(int kernel);
 
 /*
+ * wanvae_decode_tiled -- the spatially tiled decode of the diffusers PR page "Implement tiled
+ * VAE encoding/decoding for Wan model": the latent is cut into overlapping spatial tiles, each
+ * decoded on its own as wanvae_decode does, and the decoded tiles are blended where they
+ * overlap. It trades a different result for a workspace that scales with the tile, not the
+ * video.
+ *
+ *  tile_h, tile_w, stride_h, stride_w  tile size and stride in VIDEO pixels (the page's defaults
+ *           are 256 and 192), positive multiples of 16 with stride <= tile, else WANVAE_EARG.
+ *           Tiles along an axis start at latent 0, s, 2s, ... (s = stride / 16) below the latent
+ *           size and cover tile / 16 latents or what is left.
+ *  Other arguments, the output and the errors are those of wanvae_decode.
+ *
+ * Composition (the blend rule is not on the page; this reading is the linear ramp diffusers'
+ * VAEs use): in raster order, a decoded tile first takes a ramp with the tile above over its
+ * first E_v = min(H_above, H, tile_h - stride_h) rows, row y becoming
+ * above[H_above - E_v + y] * (1 - y/E_v) + own[y] * (y/E_v), then the same ramp with the tile
+ * to its left over its first E_h columns, the neighbours as already composed; the weights are
+ * float32 constants, and each product and the sum are rounded to dtype. The video takes rows
+ * [0, stride_h) and columns [0, stride_w) of every composed tile.
+ *
+ * The tiles of one tile row with equal width are decoded as one batch. Workspace
+ * (wanvae_decode_tiled_workspace_size): the rounded weights, two rows of decoded tiles, the
+ * cropped latents of one batch and the decoder's buffers for one batch.
+ */
+int wanvae_decode_tiled_workspace_size(int64_t B, int64_t T, int64_t h, int64_t w, const wanvae_tensor *weights,
+                                       int64_t n_weights, int32_t dtype, int32_t tile_h, int32_t tile_w,
+                                       int32_t stride_h, int32_t stride_w, size_t *bytes);
+int wanvae_decode_tiled(const void *z, int32_t z_dtype, int64_t B, int64_t T, int64_t h, int64_t w,
+                        const wanvae_tensor *weights, int64_t n_weights, int32_t dtype, int32_t tile_h, int32_t tile_w,
+                        int32_t stride_h, int32_t stride_w, void *video, void *workspace, size_t workspace_bytes,
+                        void *stream);
+
+/*
  * Decode pipeline switch. With on = 1 (the default) wanvae_decode runs each latent frame's
  * work as two stages on two streams of its own (made once per device, default priority):
  * conv_in, the mid block and up block 0 of frame i+1 overlap up blocks 1-3 and conv_out of

@@ -20,7 +20,7 @@ import torch
 
 import oracle
 import synthetic
-from _gpu import TORCH, dev, rounded, say, to_dev, to_np
+from _gpu import TORCH, dev, gate_bf16_scale, rounded, say, to_dev, to_np
 from video_vae_decoding_amd import wanvae
 
 pytestmark = pytest.mark.gpu
@@ -147,11 +147,8 @@ def test_decode_pipeline_matches_chunk_order_bit_for_bit(pipeline, mode):
     level 1's two input buffers three times (the wait on the second stage of chunk i-2) and
     runs the split-K level-0 convs of one chunk beside the levels above of the one before.
     The video must equal the decode in chunk order on one stream bit for bit, and match the
-    oracle: fp32 to 5e-4; bf16 with PSNR >= 40 dB and within the bf16 decode's own distance
-    from the fp32 decode (the oracle's, on these inputs: mean 1x, max 1.5x). Over seven
-    chunks the tiny bf16 decoder carries any early rounding difference into every later
-    frame; its distance from the fp32 decode is the scale such differences settle at. The
-    oracle's float32-sum variant stays closer than that on these latents for its first frames
+    oracle: fp32 to 5e-4; bf16 by gate_bf16_scale. The oracle's float32-sum variant, the
+    noise sample of the other bf16 gates, stays closer on these latents for its first frames
     only by chance (mean 0.0002 at frame 0 against 0.0025 on the T = 4 inputs above)."""
     z = synthetic.normal(8, "latents_pipe", (2, 48, 7, 3, 5))
     W = synthetic.gen_weights(16, 8, 0.1)
@@ -165,13 +162,7 @@ def test_decode_pipeline_matches_chunk_order_bit_for_bit(pipeline, mode):
     if mode == "fp32":
         gate(on, want, mode, "tiny B2 T7 fp32")
         return
-    scale = np.abs(want - oracle.decode(z, W, "fp32").astype(np.float64))
-    d = np.abs(on.astype(np.float64) - want)
-    p = oracle.psnr(on, want)
-    say("tiny B2 T7 bf16 max", d.max(), "mean", d.mean(), "psnr", p, "bf16-fp32 max", scale.max(), "mean", scale.mean())
-    assert p >= 40, p
-    assert d.mean() <= scale.mean(), (d.mean(), scale.mean())
-    assert d.max() <= 1.5 * scale.max(), (d.max(), scale.max())
+    gate_bf16_scale(on, want, oracle.decode(z, W, "fp32").astype(np.float64), "tiny B2 T7 bf16")
 
 
 def test_small32_decode_pipeline_matches_chunk_order_bit_for_bit(pipeline):

@@ -185,3 +185,35 @@ def test_decode_pipeline_switch():
             assert "0 or 1" in L.wanvae_last_error().decode()
     finally:
         W.wanvae_set_decode_pipeline(True)
+
+
+def tiled_ws(tab, n, dtype=W.BF16, B=1, T=31, h=44, w=80, tile=(256, 256), stride=(192, 192)):
+    out = ctypes.c_size_t(0)
+    rc = W.lib().wanvae_decode_tiled_workspace_size(B, T, h, w, tab, n, dtype, tile[0], tile[1], stride[0], stride[1],
+                                                    ctypes.byref(out))
+    return rc, out.value
+
+
+def test_tiled_decode_validation_and_workspace():
+    """The tiled decode's arguments are checked before anything runs, and at the page's default
+    tile (256, stride 192) its workspace for the 704 x 1280 x 121 decode is a fraction of the
+    untiled decode's (the point of tiling)."""
+    tab, n = full_table()
+    rc, tiled = tiled_ws(tab, n)
+    assert rc == W.OK
+    out = ctypes.c_size_t(0)
+    assert W.lib().wanvae_decode_workspace_size(1, 31, 44, 80, tab, n, W.BF16, ctypes.byref(out)) == W.OK
+    assert tiled < 0.6 * out.value, (tiled, out.value)
+    for tile, stride in (((250, 256), (192, 192)), ((256, 256), (0, 192)), ((256, 256), (272, 192)),
+                         ((256, 256), (192, 200))):
+        assert tiled_ws(tab, n, tile=tile, stride=stride)[0] == W.EARG
+    assert tiled_ws(tab, n, dtype=7)[0] == W.EDTYPE
+    # one tile covering the video: the untiled decode's buffers plus the tile rows
+    assert tiled_ws(tab, n, h=4, w=4, T=2, tile=(64, 64), stride=(64, 64))[0] == W.OK
+    wts = host_weights()
+    arr, m = W.tensor_table(wts)
+    _, need = tiled_ws(arr, m, dtype=W.F32, T=2, h=4, w=4, tile=(32, 32), stride=(16, 16))
+    assert W.lib().wanvae_decode_tiled(4096, W.F32, 1, 2, 4, 4, arr, m, W.F32, 32, 32, 16, 16, 4096, 4096, need - 1,
+                                       None) == W.EWORKSPACE
+    assert W.lib().wanvae_decode_tiled(None, W.F32, 1, 2, 4, 4, arr, m, W.F32, 32, 32, 16, 16, 4096, 4096, need,
+                                       None) == W.EARG

@@ -95,6 +95,25 @@ enum ConvTile {
   kTileHalo128x16x16 = 12, // 128 channels x a 16 x 16 block (small frames, with split K)
 };
 
+// One tile of the tiled decode (tiles.hip): the decoded tile cur [planes][H][W] (planes = batch x
+// colour x frame) takes the ramp with the composed tile above (its last Ev of Ha rows) over its
+// first Ev rows, then with the composed tile to the left (its last Eh of Wl columns) over its
+// first Eh columns, in place; its rows [0, keep_h) x columns [0, keep_w) go to the video
+// [planes][VH][VW] at (oy, ox). above / left may be nullptr (no ramp).
+struct TileBlendArgs {
+  void* cur;
+  const void* above;
+  const void* left;
+  int64_t planes;
+  int H, W, Ha, Ev, Wl, Eh;
+  void* video;
+  int VH, VW, oy, ox, keep_h, keep_w;
+};
+hipError_t launch_tile_blend(const TileBlendArgs& a, int dtype, hipStream_t s);
+// src [planes][h][w] (elements of esize bytes) rows y0.. x columns x0.. -> dst [planes][th][tw]
+hipError_t launch_crop(const void* src, void* dst, int esize, int64_t planes, int h, int w, int y0, int x0, int th,
+                       int tw, hipStream_t s);
+
 hipError_t launch_conv(const ConvArgs& a, int dtype, int tile, hipStream_t s);
 // whether a halo-tile kernel handles this conv (bf16, 3x3 spatial, Cin % 32; tile 10: Cout % 128 and
 // the frame epilogue; tile 11: Cout <= 16 and the video epilogue; tile 12 as tile 10)

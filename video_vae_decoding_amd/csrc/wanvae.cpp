@@ -611,6 +611,12 @@ class Decoder {
   // Lays out the workspace (measuring when ar.base is null) and, with a real base, enqueues
   // the weight preparation.
   int plan(Arena& ar, hipStream_t st) {
+    if (int rc = plan_weights(ar, st)) return rc;
+    return plan_acts(ar);
+  }
+
+  // The weights in the compute type and the kernels' layout (enqueued on st with a real base).
+  int plan_weights(Arena& ar, hipStream_t st) {
     st_ = st;
     for (const ConvSpec& c : tp_.convs) {
       ConvW& cw = cw_[c.name];
@@ -620,6 +626,18 @@ class Decoder {
     }
     for (auto& g : tp_.norms)
       if (int rc = prep_vec(ar, dt_, m_.at(g.first), g.second, gam_[g.first], st)) return rc;
+    return WANVAE_OK;
+  }
+
+  // Runs on the weights another decoder of the same parameters prepared.
+  void use_weights(const Decoder& o, hipStream_t st) {
+    cw_ = o.cw_;
+    gam_ = o.gam_;
+    st_ = st;
+  }
+
+  // Activations, caches and scratch.
+  int plan_acts(Arena& ar) {
     const int c4 = tp_.c4, c2 = tp_.c2, c1 = tp_.c1;
     up_specs(tp_.base, u_);
     const int fmax[4] = {1, T_ > 1 ? 2 : 1, T_ > 1 ? 4 : 1, T_ > 1 ? 4 : 1};
@@ -1003,6 +1021,179 @@ int wanvae_decode(const void* z, int32_t z_dtype, int64_t B, int64_t T, int64_t 
     std::unique_lock<std::mutex> lk;
     if (pipe) lk = std::unique_lock<std::mutex>(pipe->mu);
     rc = d.run(z, z_dtype, video, pipe);
+  }
+  if (!workspace) {
+    hipError_t e = hipFreeAsync(ws, st);
+    if (rc == WANVAE_OK && e != hipSuccess) rc = fail(WANVAE_EHIP, "hipFreeAsync: %s", hipGetErrorString(e));
+  }
+  return rc;
+}
+
+// ---------------------------------------------------------------- tiled decode
+
+// The tiled decode of the diffusers PR page on Wan tiling: overlapping spatial tiles of the
+// latent, each decoded on its own, composed with a linear ramp over the overlaps.
+struct TiledPlan {
+  std::vector<std::pair<int, int>> gy, gx;  // (start, size) of the tile rows / columns, latent units
+  std::vector<std::vector<int>> groups;     // columns of equal width, decoded as one batch per row
+  int F = 0;
+  size_t weights = 0, row = 0, stage = 0, acts = 0, total = 0;
+};
+
+static std::vector<std::pair<int, int>> tile_axis(int n, int tile_px, int stride_px) {
+  std::vector<std::pair<int, int>> g;
+  const int t = tile_px / 16, s = stride_px / 16;
+  for (int i = 0; i < n; i += s) g.push_back({i, std::min(t, n - i)});
+  return g;
+}
+
+static int tiled_plan(int64_t B, int64_t T, int64_t h, int64_t w, const wanvae_tensor* weights, int64_t n_weights,
+                      int32_t dtype, int32_t tile_h, int32_t tile_w, int32_t stride_h, int32_t stride_w, WeightMap& m,
+                      Topology& tp, TiledPlan& P) {
+  if (int rc = decode_validate(B, T, h, w, weights, n_weights, dtype, m, tp)) return rc;
+  const int32_t sz[4] = {tile_h, tile_w, stride_h, stride_w};
+  for (int32_t v : sz)
+    if (v < 16 || v % 16 || v > (1 << 20))
+      return fail(WANVAE_EARG, "tile %d x %d and stride %d x %d (video pixels) must be positive multiples of 16",
+                  tile_h, tile_w, stride_h, stride_w);
+  if (stride_h > tile_h || stride_w > tile_w)
+    return fail(WANVAE_EARG, "stride %d x %d must not exceed the tile %d x %d", stride_h, stride_w, tile_h, tile_w);
+  P.gy = tile_axis((int)h, tile_h, stride_h);
+  P.gx = tile_axis((int)w, tile_w, stride_w);
+  std::map<int, std::vector<int>> by_w;
+  for (int c = 0; c < (int)P.gx.size(); ++c) by_w[-P.gx[c].second].push_back(c);
+  for (auto& kv : by_w) P.groups.push_back(kv.second);
+  P.F = 4 * (int)T - 3;
+  const size_t es = esize(dtype);
+  const int thmax = P.gy[0].second;
+  {
+    Decoder wd(m, tp, dtype, (int)B, (int)T, (int)h, (int)w);
+    Arena a;
+    if (int rc = wd.plan_weights(a, nullptr)) return rc;
+    P.weights = a.used;
+  }
+  for (auto& g : P.groups) {
+    const int tw = P.gx[g[0]].second, nc = (int)g.size();
+    P.row += (size_t)B * nc * 3 * P.F * (16 * thmax) * (16 * tw) * es;
+    P.stage = std::max(P.stage, (size_t)B * nc * 48 * T * thmax * tw * 4);
+    for (size_t r = 0; r < P.gy.size(); ++r) {
+      if (r > 0 && P.gy[r].second == P.gy[r - 1].second) continue;
+      Decoder d(m, tp, dtype, (int)B * nc, (int)T, P.gy[r].second, tw);
+      Arena a;
+      if (int rc = d.plan_acts(a)) return rc;
+      P.acts = std::max(P.acts, a.used);
+    }
+  }
+  Arena a;
+  a.take(P.weights);
+  a.take(P.row);
+  a.take(P.row);
+  a.take(P.stage);
+  a.take(P.acts);
+  P.total = a.used;
+  return WANVAE_OK;
+}
+
+int wanvae_decode_tiled_workspace_size(int64_t B, int64_t T, int64_t h, int64_t w, const wanvae_tensor* weights,
+                                       int64_t n_weights, int32_t dtype, int32_t tile_h, int32_t tile_w,
+                                       int32_t stride_h, int32_t stride_w, size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(WANVAE_EARG, "bytes: NULL");
+  WeightMap m;
+  Topology tp;
+  TiledPlan P;
+  if (int rc = tiled_plan(B, T, h, w, weights, n_weights, dtype, tile_h, tile_w, stride_h, stride_w, m, tp, P)) return rc;
+  *bytes = P.total;
+  return WANVAE_OK;
+}
+
+int wanvae_decode_tiled(const void* z, int32_t z_dtype, int64_t B, int64_t T, int64_t h, int64_t w,
+                        const wanvae_tensor* weights, int64_t n_weights, int32_t dtype, int32_t tile_h, int32_t tile_w,
+                        int32_t stride_h, int32_t stride_w, void* video, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  g_err.clear();
+  WeightMap m;
+  Topology tp;
+  TiledPlan P;
+  if (int rc = tiled_plan(B, T, h, w, weights, n_weights, dtype, tile_h, tile_w, stride_h, stride_w, m, tp, P)) return rc;
+  if (int rc = check_dtype(z_dtype, "z_dtype")) return rc;
+  if (!z || !video) return fail(WANVAE_EARG, "z and video must not be NULL");
+  if (workspace && workspace_bytes < P.total)
+    return fail(WANVAE_EWORKSPACE, "workspace of %zu bytes, the tiled decode needs %zu", workspace_bytes, P.total);
+  hipStream_t st = (hipStream_t)stream;
+  void* ws = workspace;
+  if (!ws) HIP_TRY(hipMallocAsync(&ws, P.total, st));
+  int rc = WANVAE_OK;
+  {
+    Arena ar;
+    ar.base = (char*)ws;
+    Decoder wd(m, tp, dtype, (int)B, (int)T, (int)h, (int)w);
+    rc = wd.plan_weights(ar, st);
+    char* rowbuf[2] = {(char*)ar.take(P.row), (char*)ar.take(P.row)};
+    char* stage = (char*)ar.take(P.stage);
+    char* acts = (char*)ar.take(P.acts);
+    Pipe* pipe = nullptr;
+    if (rc == WANVAE_OK && T > 1 && g_pipeline.load(std::memory_order_relaxed)) rc = pipe_for_device(&pipe);
+    std::unique_lock<std::mutex> lk;
+    if (pipe) lk = std::unique_lock<std::mutex>(pipe->mu);
+    const size_t es = esize(dtype), zes = esize(z_dtype);
+    const int VH = 16 * (int)h, VW = 16 * (int)w;
+    const int Ev_max = tile_h - stride_h, Eh_max = tile_w - stride_w;
+    std::vector<char*> prev(P.gx.size(), nullptr), cur(P.gx.size(), nullptr);
+    int prev_H = 0;
+    for (size_t r = 0; r < P.gy.size() && rc == WANVAE_OK; ++r) {
+      const int y0 = P.gy[r].first, th = P.gy[r].second, H = 16 * th;
+      // decode the row's tiles, one batch per group of equal width (tile k of a group is batch
+      // elements k*B .. k*B + B - 1 of that decode)
+      size_t off = 0;
+      for (const auto& g : P.groups) {
+        if (rc != WANVAE_OK) break;
+        const int tw = P.gx[g[0]].second, nc = (int)g.size(), W = 16 * tw;
+        const size_t zt = (size_t)B * 48 * T * th * tw;  // latent elements of one tile
+        const size_t vt = (size_t)B * 3 * P.F * H * W;   // video elements of one tile
+        for (int k = 0; k < nc && rc == WANVAE_OK; ++k) {
+          hipEvent_t e0 = prof_start(st);
+          hipError_t e = launch_crop(z, stage + k * zt * zes, (int)zes, B * 48 * T, (int)h, (int)w, y0,
+                                     P.gx[g[k]].first, th, tw, st);
+          if (e != hipSuccess) rc = fail(WANVAE_EHIP, "tile crop: %s", hipGetErrorString(e));
+          prof_stop(e0, WANVAE_KOTHER, 0, 2.0 * zt * zes, st);
+        }
+        if (rc != WANVAE_OK) break;
+        Decoder d(m, tp, dtype, (int)B * nc, (int)T, th, tw);
+        d.use_weights(wd, st);
+        Arena aa;
+        aa.base = acts;
+        char* out = rowbuf[r & 1] + off;
+        rc = d.plan_acts(aa);
+        if (rc == WANVAE_OK) rc = d.run(stage, z_dtype, out, pipe);
+        for (int k = 0; k < nc; ++k) cur[g[k]] = out + k * vt * es;
+        off += nc * vt * es;
+      }
+      // compose the row's tiles in order
+      for (size_t c = 0; c < P.gx.size() && rc == WANVAE_OK; ++c) {
+        const int x0 = P.gx[c].first, tw = P.gx[c].second, W = 16 * tw;
+        TileBlendArgs a;
+        a.cur = cur[c];
+        a.above = r > 0 ? prev[c] : nullptr;
+        a.left = c > 0 ? cur[c - 1] : nullptr;
+        a.planes = B * 3 * P.F;
+        a.H = H, a.W = W;
+        a.Ha = prev_H;
+        a.Ev = r > 0 ? std::min({prev_H, H, Ev_max}) : 0;
+        a.Wl = c > 0 ? 16 * P.gx[c - 1].second : 0;
+        a.Eh = c > 0 ? std::min({a.Wl, W, Eh_max}) : 0;
+        a.video = video;
+        a.VH = VH, a.VW = VW;
+        a.oy = 16 * y0, a.ox = 16 * x0;
+        a.keep_h = std::min(stride_h, H), a.keep_w = std::min(stride_w, W);
+        hipEvent_t e0 = prof_start(st);
+        hipError_t e = launch_tile_blend(a, dtype, st);
+        if (e != hipSuccess) rc = fail(WANVAE_EHIP, "tile blend: %s", hipGetErrorString(e));
+        prof_stop(e0, WANVAE_KOTHER, 0, 3.0 * a.planes * H * W * es, st);
+      }
+      std::swap(prev, cur);
+      prev_H = H;
+    }
   }
   if (!workspace) {
     hipError_t e = hipFreeAsync(ws, st);

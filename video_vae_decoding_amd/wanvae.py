@@ -64,10 +64,13 @@ def lib() -> ctypes.CDLL:
         L.wanvae_version.argtypes = []
         L.wanvae_set_conv_kernel.argtypes = [ctypes.c_int]
         L.wanvae_set_decode_pipeline.argtypes = [ctypes.c_int]
+        L.wanvae_decode_tiled_workspace_size.argtypes = [i64, i64, i64, i64, T, i64, i32, i32, i32, i32, i32,
+                                                         ctypes.POINTER(sz)]
+        L.wanvae_decode_tiled.argtypes = [vp, i32, i64, i64, i64, i64, T, i64, i32, i32, i32, i32, i32, vp, vp, sz, vp]
         for f in ("wanvae_decode_workspace_size", "wanvae_decode", "wanvae_causal_conv3d_workspace_size",
                   "wanvae_causal_conv3d", "wanvae_attn_block_workspace_size", "wanvae_attn_block", "wanvae_version",
                   "wanvae_profile_enable", "wanvae_profile_read", "wanvae_set_conv_kernel",
-                  "wanvae_set_decode_pipeline"):
+                  "wanvae_set_decode_pipeline", "wanvae_decode_tiled_workspace_size", "wanvae_decode_tiled"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -147,6 +150,38 @@ def wanvae_decode(z: torch.Tensor, weights: Mapping[str, torch.Tensor], dtype=to
 
 
 decode = wanvae_decode
+
+
+def decode_tiled_workspace_size(B, T, h, w, weights: Mapping[str, torch.Tensor], dtype=torch.float32,
+                                tile=(256, 256), stride=(192, 192)) -> int:
+    arr, n = tensor_table(weights)
+    out = ctypes.c_size_t(0)
+    check(lib().wanvae_decode_tiled_workspace_size(B, T, h, w, arr, n, dtype_code(dtype), tile[0], tile[1], stride[0],
+                                                   stride[1], ctypes.byref(out)))
+    return out.value
+
+
+def wanvae_decode_tiled(z: torch.Tensor, weights: Mapping[str, torch.Tensor], dtype=torch.float32,
+                        tile=(256, 256), stride=(192, 192), video: torch.Tensor | None = None,
+                        workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """The spatially tiled decode: overlapping tiles of tile[0] x tile[1] video pixels every
+    stride[0] x stride[1], each decoded on its own, blended where they overlap."""
+    dt = dtype_code(dtype)
+    if z.dim() != 5:
+        raise ValueError(f"z must be [B, 48, T, h, w], got {tuple(z.shape)}")
+    B, C, T, h, w = z.shape
+    z = z.contiguous()
+    arr, n = tensor_table(weights)
+    need = decode_tiled_workspace_size(B, T, h, w, weights, dtype, tile, stride)
+    if video is None:
+        video = torch.empty((B, 3, 4 * T - 3, 16 * h, 16 * w), dtype=dtype, device=z.device)
+    ws = _workspace(need, z.device, workspace)
+    check(lib().wanvae_decode_tiled(z.data_ptr(), dtype_code(z.dtype), B, T, h, w, arr, n, dt, tile[0], tile[1],
+                                    stride[0], stride[1], video.data_ptr(), ws.data_ptr(), need, _stream(z.device)))
+    return video
+
+
+decode_tiled = wanvae_decode_tiled
 
 
 def conv_workspace_size(B, Cin, Cout, t, h, w, n_cache, layout, dtype) -> int:
