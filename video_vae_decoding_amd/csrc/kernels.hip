@@ -1275,8 +1275,9 @@ __global__ void __launch_bounds__(256) k_norm(const NormArgs a) {
 
 // Bandwidth-oriented version: a position's C channels are spread over LPP lanes, each lane
 // holding VPL 16-byte vectors; a wave covers 64 / LPP positions per round and R rounds, all
-// loads issued before the sums are reduced (xor shuffles within the LPP lanes).
-template <typename T, int LPP, int VPL, int R>
+// loads issued before the sums are reduced (xor shuffles within the LPP lanes). bf16 rounds
+// two values per conversion instruction, and the last rounding is the packing store's.
+template <typename T, int LPP, int VPL, int R, bool SILU>
 __global__ void __launch_bounds__(256) k_norm_v(const NormArgs a) {
   using X = Elem<T>;
   constexpr int EV = 16 / (int)sizeof(T);  // elements per 16-byte vector
@@ -1336,23 +1337,37 @@ __global__ void __launch_bounds__(256) k_norm_v(const NormArgs a) {
     for (int v = 0; v < VPL; ++v) {
       const int c0 = (v * LPP + li) * EV;
       float o[EV];
+      if constexpr (sizeof(T) == 2) {
+        // bf16: reciprocal multiply, hardware exp and reciprocal; each differs from the
+        // correctly rounded fp32 operation by a few fp32 ulp, below the bf16 rounding
+        auto round2 = [](float& p, float& q) {
+          const uint32_t w = pack2_bf16(p, q);
+          p = __uint_as_float(w << 16);
+          q = __uint_as_float(w & 0xffff0000u);
+        };
 #pragma unroll
-      for (int e = 0; e < EV; ++e) {
-        float u;
-        if constexpr (sizeof(T) == 2) {
-          // bf16: reciprocal multiply, hardware exp2 and reciprocal; each differs from the
-          // correctly rounded fp32 operation by a few fp32 ulp, below the bf16 rounding
-          u = X::R(val[v][e] * inv);
-          u = X::R(u * a.sqrtC);
-          u = X::R(u * g[v][e]);
-          if (a.silu) u = X::R(u * __builtin_amdgcn_rcpf(1.f + __expf(-u)));
-        } else {
-          u = val[v][e] / d;
+        for (int e = 0; e < EV; e += 2) {
+          float u0 = val[v][e] * inv, u1 = val[v][e + 1] * inv;
+          round2(u0, u1);
+          u0 *= a.sqrtC, u1 *= a.sqrtC;
+          round2(u0, u1);
+          u0 *= g[v][e], u1 *= g[v][e + 1];
+          if constexpr (SILU) {
+            round2(u0, u1);
+            u0 = u0 * __builtin_amdgcn_rcpf(1.f + __expf(-u0));
+            u1 = u1 * __builtin_amdgcn_rcpf(1.f + __expf(-u1));
+          }
+          o[e] = u0, o[e + 1] = u1;  // rounded by the packing store
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < EV; ++e) {
+          float u = val[v][e] / d;
           u = u * a.sqrtC;
           u = u * g[v][e];
-          if (a.silu) u = u / (1.f + expf(-u));
+          if constexpr (SILU) u = u / (1.f + expf(-u));
+          o[e] = u;
         }
-        o[e] = u;
       }
       if constexpr (sizeof(T) == 2) {
         *(uint4*)(outp[r] + c0) = pack8_bf16(o);
@@ -1733,8 +1748,11 @@ template <typename T, int LPP, int VPL>
 static hipError_t norm_v_go(const NormArgs& a, hipStream_t s) {
   constexpr int R = 4;
   const int per_block = 4 * (64 / LPP) * R;
-  hipLaunchKernelGGL((k_norm_v<T, LPP, VPL, R>), dim3((unsigned)((a.HW + per_block - 1) / per_block), (unsigned)(a.F * a.B)),
-                     dim3(256), 0, s, a);
+  const dim3 grid((unsigned)((a.HW + per_block - 1) / per_block), (unsigned)(a.F * a.B));
+  if (a.silu)
+    hipLaunchKernelGGL((k_norm_v<T, LPP, VPL, R, true>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_norm_v<T, LPP, VPL, R, false>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
