@@ -1382,8 +1382,9 @@ __global__ void __launch_bounds__(256) k_norm_v(const NormArgs a) {
 //
 // One workgroup: 32 queries (2 tiles of 16) of one frame, NW waves; wave w owns head dims
 // [w*DW, (w+1)*DW). Per block of 32 keys each wave computes its partial S^T = K Q^T over its
-// dims (MFMA, Q fragments held in registers), the partials are summed through LDS (wave
-// order fixed, so the result is deterministic), then every wave runs the online softmax on
+// dims (MFMA, Q fragments held in registers), the partials are summed through LDS (each
+// wave sums 1/NW of the tile over all waves, in wave order, so the result is deterministic;
+// then every wave reads the whole sum), then every wave runs the online softmax on
 // the full scores and accumulates O^T += V^T P for its own dims. S^T's accumulator layout
 // (keys 4g..4g+3 of each 16-key tile in lane group g, one query per lane) is directly the
 // k layout of P as the B operand of the PV MFMA; V^T is read with the same key order.
@@ -1394,7 +1395,8 @@ __global__ void __launch_bounds__(64 * NW) k_attn(const AttnArgs a) {
   constexpr int KS = BF ? 32 : 16;  // head dims per S MFMA step
   constexpr int NKS = DW / KS;
   constexpr int NDT = DW / 16;       // 16-dim tiles of O per wave
-  __shared__ f32x4_t red[2][NW][4][64];
+  __shared__ f32x4_t red[2][NW][4][64];  // each wave's partial S^T tile (1,024 floats)
+  __shared__ f32x4_t rsum[2][4][64];     // the summed tile
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int l16 = lane & 15, g = lane >> 4;
@@ -1442,15 +1444,29 @@ __global__ void __launch_bounds__(64 * NW) k_attn(const AttnArgs a) {
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) red[par][w][kt * 2 + qt][lane] = s[kt][qt];
     __syncthreads();
+    {
+      // reduce-scatter: wave w sums floats [w * FPW, (w + 1) * FPW) of the tile over the waves,
+      // in wave order, and every wave then reads the whole summed tile
+      constexpr int FPW = 1024 / NW, FPL = FPW / 64;
+      static_assert(FPL * 64 * NW == 1024, "the tile splits evenly over the waves' lanes");
+      const float* rf = (const float*)&red[par][0][0][0];
+      float* sf = (float*)&rsum[par][0][0];
+      const int f0 = w * FPW + lane * FPL;
+      float acc[FPL];
+#pragma unroll
+      for (int e = 0; e < FPL; ++e) acc[e] = rf[f0 + e];
+#pragma unroll
+      for (int ww = 1; ww < NW; ++ww)
+#pragma unroll
+        for (int e = 0; e < FPL; ++e) acc[e] += rf[ww * 1024 + f0 + e];
+#pragma unroll
+      for (int e = 0; e < FPL; ++e) sf[f0 + e] = acc[e];
+    }
+    __syncthreads();
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        f32x4_t t = red[par][0][kt * 2 + qt][lane];
-#pragma unroll
-        for (int ww = 1; ww < NW; ++ww) t += red[par][ww][kt * 2 + qt][lane];
-        s[kt][qt] = t;
-      }
+      for (int qt = 0; qt < 2; ++qt) s[kt][qt] = rsum[par][kt * 2 + qt][lane];
     // online softmax; key of element e in tile kt: kv0 + kt*16 + 4g + e
     float p[2][2][4];
 #pragma unroll
@@ -1812,7 +1828,7 @@ hipError_t launch_attn(const AttnArgs& a, int dtype, hipStream_t s) {
       case 256: return attn_go<bf16_t, 4, 64>(a, s);
       case 384: return attn_go<bf16_t, 4, 96>(a, s);
       case 512: return attn_go<bf16_t, 4, 128>(a, s);
-      case 1024: return attn_go<bf16_t, 4, 256>(a, s);
+      case 1024: return attn_go<bf16_t, 8, 128>(a, s);
     }
   } else {
     switch (a.C) {
