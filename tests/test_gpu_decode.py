@@ -180,6 +180,47 @@ def test_small32_decode_pipeline_matches_chunk_order_bit_for_bit(pipeline):
     assert torch.isfinite(on).all()
 
 
+def test_concurrent_decodes_on_two_threads_and_streams():
+    """Two host threads decode at once, each on a stream of its own with its own workspace: the
+    library serialises their enqueueing on the device's two pipeline streams, each call stays
+    ordered on its caller's stream, and both videos equal the same decode run alone, bit for
+    bit (bf16, B = 1, T = 5, base 32)."""
+    import threading
+    cfg = synthetic.DECODE_CONFIGS["small32"]
+    zs = [synthetic.normal(20 + i, "latents_threads", (1, 48, 5, cfg.h, cfg.w)) for i in range(2)]
+    W = cfg.weights()
+    Wt = {k: torch.from_numpy(v).to(dev()) for k, v in W.items()}
+    zt = [torch.from_numpy(z).to(dev()) for z in zs]
+    alone = []
+    for z in zt:
+        alone.append(wanvae.wanvae_decode(z, Wt, torch.bfloat16))
+        torch.cuda.synchronize()
+    out = [None, None]
+    errors = []
+
+    def run(i):
+        try:
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                for _ in range(3):
+                    out[i] = wanvae.wanvae_decode(zt[i], Wt, torch.bfloat16)
+                st.synchronize()
+        except Exception as e:  # noqa: BLE001
+            errors.append(e)
+
+    say("two threads decoding small32 T5 at once")
+    th = [threading.Thread(target=run, args=(i,)) for i in range(2)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in th)
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for i in range(2):
+        assert torch.equal(out[i], alone[i])
+
+
 def test_unpatchify_channel_map_and_clamp_are_exact(tiny):
     """conv_out weights zero, biases c: every pixel of colour k at row offset i and column
     offset j equals clamp(bias[4k + 2j + i]), bit for bit."""
