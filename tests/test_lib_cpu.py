@@ -217,3 +217,15 @@ def test_tiled_decode_validation_and_workspace():
                                        None) == W.EWORKSPACE
     assert W.lib().wanvae_decode_tiled(None, W.F32, 1, 2, 4, 4, arr, m, W.F32, 32, 32, 16, 16, 4096, 4096, need,
                                        None) == W.EARG
+
+
+def test_oversized_latent_is_eshape_before_any_launch():
+    """A latent past the library's size limit (B * h * w * 4096 above 2^31: the kernels use
+    32-bit offsets inside a frame) is rejected before anything runs, as are zero sizes."""
+    wts = host_weights()
+    assert call_decode(wts, h=1000, w=1000) == W.ESHAPE
+    assert "too large" in W.lib().wanvae_last_error().decode()
+    assert call_decode(wts, B=0) == W.ESHAPE
+    assert call_decode(wts, w=0) == W.ESHAPE
+    tab, n = full_table()
+    assert tiled_ws(tab, n, h=1000, w=1000)[0] == W.ESHAPE
