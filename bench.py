@@ -59,13 +59,59 @@ def cpu_baseline(cfg, W, mode="bf16"):
     v = oracle.decode(np.ascontiguousarray(z), W, mode)
     dt = time.perf_counter() - t0
     frac = (ch * cw) / (cfg.h * cfg.w)
-    cores = len(os.sched_getaffinity(0))
-    threads = os.environ.get("OPENBLAS_NUM_THREADS") or os.environ.get("OMP_NUM_THREADS") or str(cores)
-    return {"value": frac * v.shape[2] / dt, "unit": "frames/s", "cores": int(threads) if threads.isdigit() else cores,
+    return {"value": frac * v.shape[2] / dt, "unit": "frames/s", "cores": _cores(),
             "kind": "oracle", "seconds": round(dt, 2),
             "sample": f"oracle.decode ({mode} mode, float64 sums) of latent frame 0 on a {ch}x{cw} crop of the "
                       f"[{cfg.B},48,{cfg.T},{cfg.h},{cfg.w}] latents (batch element 0): 1 video frame of "
                       f"{16 * ch}x{16 * cw} = 1/16 of a {16 * cfg.h}x{16 * cfg.w} frame; value = (1/16 frame) / seconds"}
+
+
+def _cores():
+    cores = len(os.sched_getaffinity(0))
+    threads = os.environ.get("OPENBLAS_NUM_THREADS") or os.environ.get("OMP_NUM_THREADS") or str(cores)
+    return int(threads) if threads.isdigit() else cores
+
+
+def cpu_baseline_conv(cfg):
+    """The CPU oracle's causal conv (bf16 rounding, float64 sums) on the workload's tensors,
+    cropped to at most 88 x 160 positions per frame, in TFLOP/s of algorithmic work."""
+    import oracle
+    x, cache, w, b = cfg.tensors()
+    hh, ww = min(cfg.h, 88), min(cfg.w, 160)
+    R = oracle.round_bf16
+    xs = R(np.ascontiguousarray(x[:, :, :, :hh, :ww]))
+    cs = R(np.ascontiguousarray(cache[:, :, :, :hh, :ww])) if cfg.n_cache else None
+    P = oracle.Prec("bf16")
+    t0 = time.perf_counter()
+    oracle.causal_conv(xs, R(w), R(b), cs, P)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * cfg.t * hh * ww * cfg.C * cfg.C * 27
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": _cores(), "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"oracle.causal_conv (bf16 mode, float64 sums) on the workload's x and {cfg.n_cache} cached frames "
+                      f"cropped to {cfg.t} frames of {hh}x{ww}: {flops / 1e9:.1f} GFLOP"}
+
+
+def cpu_baseline_attn(cfg):
+    """The CPU oracle's attention block (bf16 rounding, float64 sums) on frame 0 of the workload
+    at its first R query positions (every key and value used), in TFLOP/s of the block's
+    algorithmic work for those R queries."""
+    import oracle
+    T = cfg.tensors()
+    S, C = cfg.h * cfg.w, cfg.C
+    rows = np.arange(min(S, 4096))
+    R = oracle.round_bf16
+    frame = R(np.ascontiguousarray(T["x"][0, :, 0]))
+    par = [R(T[k]) for k in ("gamma", "qkv_w", "qkv_b", "proj_w", "proj_b")]
+    t0 = time.perf_counter()
+    oracle.attention_rows(frame, *par, oracle.Prec("bf16"), rows)
+    dt = time.perf_counter() - t0
+    flops = len(rows) * (4.0 * S * C + 8.0 * C * C)
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": _cores(), "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"oracle.attention_rows (bf16 mode, float64 sums) on frame 0 ({S} positions, C = {C}) at its first "
+                      f"{len(rows)} queries; value = the block's work for those queries ({flops / 1e9:.1f} GFLOP) / seconds "
+                      "(the oracle also projects k and v for every position, not counted)"}
 
 
 def stored_traffic():
@@ -116,8 +162,9 @@ def kernel_classes(prof, steps):
 
 
 def single_op(name, args):
-    """One causal conv (C2a, C2b) or the attention block (C3) in bf16, NTHWC operands resident
-    in HBM; value = the op's algorithmic TFLOP/s over the timed wall time."""
+    """One causal conv (C2a, C2b) or the attention block (C3, and at the 720p latent frame) in
+    bf16, NTHWC operands resident in HBM; value = the op's algorithmic TFLOP/s over the timed
+    wall time; cpu_baseline = the oracle's rate on a bounded sample of the same op."""
     import torch
 
     import synthetic
@@ -172,6 +219,9 @@ def single_op(name, args):
                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
                         "launches": main_k["launches"], "avg_launch_ms": round(main_k["ms"] / max(1, main_k["launches"]), 4)},
            "kernels": kernel_classes(prof, args.steps)}
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on its sample ...")
+        out["cpu_baseline"] = cpu_baseline_conv(cfg) if kind == "conv" else cpu_baseline_attn(cfg)
     print(json.dumps(out), flush=True)
 
 
