@@ -1,6 +1,7 @@
 // Host side of the MI355X Wan2.2 TI2V-5B VAE decoder: the C ABI of include/wanvae.h,
 // argument validation (done before anything is launched), topology inference from the
-// parameter shapes, the workspace plan, and the chunk loop that enqueues the kernels.
+// parameter shapes, the workspace plan, the chunk loop that enqueues the kernels (two
+// stages per chunk, pipelined over two streams), and the spatially tiled decode.
 //
 // What is computed follows FastVideo's "wan22_vae_decode reference.py" page: post_quant_conv
 // over all latent frames, then one latent frame per chunk through conv_in, the mid block
