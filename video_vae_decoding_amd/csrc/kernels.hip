@@ -304,37 +304,43 @@ __global__ void __launch_bounds__(256) k_conv(const ConvArgs a) {
 #pragma unroll
     for (int ip = 0; ip < TPN; ++ip) acc[ic][ip] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int buf) {
+  // A step is two halves of 64 bytes per row. Fragments come in two register sets: the second
+  // half's are read while the first half's MFMAs run, and the next step's first half (after
+  // the barrier that publishes it) while the second half's run.
+  uint4 wf[2][TCN], af[2][TPN];
+  auto read_half = [&](int set, int buf, int sub) {
     const char* sw = smem + buf * STAGE + (wc * WC) * ROW;
     const char* sa = smem + buf * STAGE + TC * ROW + (wp * WP) * ROW;
+    const int off = (sub * 4 + (lane >> 4)) * 16;
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int off = (sub * 4 + (lane >> 4)) * 16;
-      uint4 wf[TCN], af[TPN];
+    for (int ic = 0; ic < TCN; ++ic) wf[set][ic] = *(const uint4*)(sw + (ic * 16 + (lane & 15)) * ROW + off);
 #pragma unroll
-      for (int ic = 0; ic < TCN; ++ic) wf[ic] = *(const uint4*)(sw + (ic * 16 + (lane & 15)) * ROW + off);
+    for (int ip = 0; ip < TPN; ++ip) af[set][ip] = *(const uint4*)(sa + (ip * 16 + (lane & 15)) * ROW + off);
+  };
+  auto mfma_half = [&](int set) {
 #pragma unroll
-      for (int ip = 0; ip < TPN; ++ip) af[ip] = *(const uint4*)(sa + (ip * 16 + (lane & 15)) * ROW + off);
+    for (int ic = 0; ic < TCN; ++ic)
 #pragma unroll
-      for (int ic = 0; ic < TCN; ++ic)
-#pragma unroll
-        for (int ip = 0; ip < TPN; ++ip) Mma<T>::run(acc[ic][ip], wf[ic], af[ip]);
-    }
+      for (int ip = 0; ip < TPN; ++ip) Mma<T>::run(acc[ic][ip], wf[set][ic], af[set][ip]);
   };
 
   set_tap();
   gload();
   sstore(0);
   __syncthreads();
+  read_half(0, 0, 0);
   for (int s = 0; s < steps; ++s) {
     const int buf = s & 1;
     if (s + 1 < steps) {
       advance();
       gload();
     }
-    compute(buf);
+    read_half(1, buf, 1);
+    mfma_half(0);
     if (s + 1 < steps) sstore(buf ^ 1);
     __syncthreads();
+    if (s + 1 < steps) read_half(0, buf ^ 1, 0);
+    mfma_half(1);
   }
 
 #pragma unroll
