@@ -340,7 +340,7 @@ def main():
                    "accumulate": "fp32", "pipeline": not args.no_pipeline, "workspace_bytes": ws.numel()},
         "roofline": {"bound": "mfma",
                      "kernel": ("conv (k_conv_halo for the 3x3 convs, k_conv_dma for the rest; all launches of a decode)"
-                                if mode == "bf16" else "conv (k_conv, fp32 MFMA; all launches of a decode)"),
+                                if mode == "bf16" else "conv (k_conv_dma, fp32 MFMA; k_conv for conv_out; all launches of a decode)"),
                      "achieved": round(conv_tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(conv_tflops / peak, 4), "traffic": stored_traffic() if default else None,
                      "launches": conv["launches"], "avg_launch_ms": round(conv["ms"] / max(1, conv["launches"]), 4),

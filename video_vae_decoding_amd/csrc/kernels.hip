@@ -447,14 +447,14 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
 }
 
-template <int TC, int TP, int WGC, int WGP, int STAGES, int MINB, bool ALIGNED, bool RB2 = false>
+template <int TC, int TP, int WGC, int WGP, int STAGES, int MINB, bool ALIGNED, bool RB2 = false, typename T = bf16_t>
 __global__ void __launch_bounds__(64 * WGC * WGP, MINB) k_conv_dma(const ConvArgs a) {
-  // ALIGNED: Cin % 32 == 0, Cout % TC == 0 and TC >= 16 * waves, so every weight row a wave
+  // ALIGNED: Cin % KS == 0, Cout % TC == 0 and TC >= 16 * waves, so every weight row a wave
   // loads exists and no 16-byte chunk straddles the end of a pixel: the per-step loads need
-  // no selects.
-  using T = bf16_t;
+  // no selects. T is bf16_t (32 channels per K step) or float (16).
   constexpr int NWAVE = WGC * WGP;
-  constexpr int ROWB = 64;                       // 32 bf16 per row per step
+  constexpr int ROWB = 64;                       // bytes per row per step
+  constexpr int ES = (int)sizeof(T), KS = ROWB / ES, CE = 16 / ES;  // element size, channels per step, per chunk
   constexpr int WC = TC / WGC, WP = TP / WGP;    // wave tile
   constexpr int TCN = WC / 16, TPN = WP / 16;
   // DMA instructions per wave per step (each moves 16 rows): W, A. When the W tile has fewer
@@ -487,7 +487,7 @@ __global__ void __launch_bounds__(64 * WGC * WGP, MINB) k_conv_dma(const ConvArg
   const int ct = bid % nct, pt = bid / nct;
   const int c0 = ct * TC, m0 = pt * TP;
   const int khw = a.kh * a.kw, taps = a.kt * khw;
-  const int csteps = (a.Cin + 31) / 32;
+  const int csteps = (a.Cin + KS - 1) / KS;
   const int all_steps = taps * csteps;
   const int s_begin = (int)((int64_t)all_steps * kz / a.ksplit);
   const int steps = (int)((int64_t)all_steps * (kz + 1) / a.ksplit) - s_begin;
@@ -509,8 +509,8 @@ __global__ void __launch_bounds__(64 * WGC * WGP, MINB) k_conv_dma(const ConvArg
   for (int i = 0; i < NIW; ++i) {
     const int r = (wave * NIW + i) * 16;
     const int n = c0 + r + lrow;
-    woffl[i] = (uint32_t)(((int64_t)(r + lrow) * Ktot + lchunk * 8) * 2);
-    wrow[i] = (r < TC && n < a.Cout) ? (const T*)a.w + n * Ktot + lchunk * 8 : nullptr;
+    woffl[i] = (uint32_t)(((int64_t)(r + lrow) * Ktot + lchunk * CE) * ES);
+    wrow[i] = (r < TC && n < a.Cout) ? (const T*)a.w + n * Ktot + lchunk * CE : nullptr;
     wdst[i] = r < TC ? r * ROWB : SW + SA;
   }
   // A rows: position, and its frame for each time tap
@@ -542,7 +542,7 @@ __global__ void __launch_bounds__(64 * WGC * WGP, MINB) k_conv_dma(const ConvArg
     }
   }
 
-  // issue cursor: the next K step to load (taps major, 32-channel blocks minor), advanced
+  // issue cursor: the next K step to load (taps major, KS-channel blocks minor), advanced
   // without divisions; per tap each A row's source pointer (the zero page where the tap reads
   // zeros: padding, a missing history frame, a position past the end)
   const char* ap[NIA];
@@ -569,7 +569,7 @@ __global__ void __launch_bounds__(64 * WGC * WGP, MINB) k_conv_dma(const ConvArg
         xx = rx[i] + cdx - pw;
         ok = ok && yy >= 0 && yy < a.Hin && xx >= 0 && xx < a.Win;
       }
-      ap[i] = ok ? (const char*)(base + ((int64_t)yy * a.Win + xx) * a.Cin + lchunk * 8) : zero + lchunk * 16;
+      ap[i] = ok ? (const char*)(base + ((int64_t)yy * a.Win + xx) * a.Cin + lchunk * CE) : zero + lchunk * 16;
     }
   };
   auto advance = [&]() {
@@ -587,18 +587,18 @@ __global__ void __launch_bounds__(64 * WGC * WGP, MINB) k_conv_dma(const ConvArg
     }
   };
   auto issue = [&](char* buf) {
-    const int cb = ccs * 32;
+    const int cb = ccs * KS;
     if constexpr (ALIGNED) {
-      const char* wstep = wtile + (woff + cb) * 2;
+      const char* wstep = wtile + (woff + cb) * ES;
 #pragma unroll
       for (int i = 0; i < NIW; ++i)
         __builtin_amdgcn_global_load_lds((const void*)(wstep + woffl[i]), LDS_PTR(buf + wdst[i]), 16, 0, 0);
 #pragma unroll
       for (int i = 0; i < NIA; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(ap[i] + cb * 2), LDS_PTR(buf + SW + (wave * NIA + i) * 1024), 16,
+        __builtin_amdgcn_global_load_lds((const void*)(ap[i] + cb * ES), LDS_PTR(buf + SW + (wave * NIA + i) * 1024), 16,
                                          0, 0);
     } else {
-      const bool cok = cb + lchunk * 8 < a.Cin;
+      const bool cok = cb + lchunk * CE < a.Cin;
 #pragma unroll
       for (int i = 0; i < NIW; ++i) {
         const char* src = (cok && wrow[i]) ? (const char*)(wrow[i] + woff + cb) : zero;
@@ -606,7 +606,7 @@ __global__ void __launch_bounds__(64 * WGC * WGP, MINB) k_conv_dma(const ConvArg
       }
 #pragma unroll
       for (int i = 0; i < NIA; ++i) {
-        const char* src = cok ? ap[i] + cb * 2 : zero;
+        const char* src = cok ? ap[i] + cb * ES : zero;
         __builtin_amdgcn_global_load_lds((const void*)src, LDS_PTR(buf + SW + (wave * NIA + i) * 1024), 16, 0, 0);
       }
     }
@@ -753,6 +753,29 @@ __global__ void __launch_bounds__(64 * WGC * WGP, MINB) k_conv_dma(const ConvArg
         if (m < M && c < a.Cout)
           *(float4*)(a.part + ((int64_t)kz * M + m) * a.Cout + c) =
               make_float4(acc[ic][ip][0], acc[ic][ip][1], acc[ic][ip][2], acc[ic][ip][3]);
+      }
+    }
+    return;
+  }
+  if constexpr (ES == 4) {
+    // fp32: each lane finishes its own 4 channels of each position (conv_epilogue: every mode)
+#pragma unroll
+    for (int ip = 0; ip < TPN; ++ip) {
+      const int m = m0 + wp * WP + ip * 16 + (lane & 15);
+      if (m >= M) continue;
+      const int x = m % a.Wo;
+      int q = m / a.Wo;
+      const int y = q % a.Ho;
+      q /= a.Ho;
+      const int b = q % a.B, t = q / a.B;
+#pragma unroll
+      for (int ic = 0; ic < TCN; ++ic) {
+        const int c = c0 + wc * WC + ic * 16 + 4 * (lane >> 4);
+        if (c >= a.Cout) continue;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[ic][ip][e] + (c + e < a.Cout ? a.bias[c + e] : 0.f);
+        conv_epilogue<T>(a, t, b, y, x, c, v);
       }
     }
     return;
@@ -1689,27 +1712,28 @@ static hipError_t conv_go(const ConvArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int TC, int TP, int WGC, int WGP, int STAGES, int MINB, bool RB2 = false>
+template <int TC, int TP, int WGC, int WGP, int STAGES, int MINB, bool RB2 = false, typename T = bf16_t>
 static hipError_t conv_dma_launch(const ConvArgs& a, hipStream_t s) {
   const int64_t M = (int64_t)a.F * a.B * a.Ho * a.Wo;
   const int64_t blocks = ((a.Cout + TC - 1) / TC) * ((M + TP - 1) / TP) * a.ksplit;
+  constexpr int KS = 64 / (int)sizeof(T);  // channels per K step
   // the aligned path loads every wave's weight rows unconditionally: only where they all lie
   // in the tile (16 rows per wave and instruction), not on the 16-channel tile
   if constexpr (TC >= 16 * WGC * WGP) {
-    if (a.Cin % 32 == 0 && a.Cout % TC == 0) {
-      hipLaunchKernelGGL((k_conv_dma<TC, TP, WGC, WGP, STAGES, MINB, true, RB2>), dim3((unsigned)blocks),
+    if (a.Cin % KS == 0 && a.Cout % TC == 0) {
+      hipLaunchKernelGGL((k_conv_dma<TC, TP, WGC, WGP, STAGES, MINB, true, RB2, T>), dim3((unsigned)blocks),
                          dim3(64 * WGC * WGP), 0, s, a);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((k_conv_dma<TC, TP, WGC, WGP, STAGES, MINB, false, RB2>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((k_conv_dma<TC, TP, WGC, WGP, STAGES, MINB, false, RB2, T>), dim3((unsigned)blocks),
                      dim3(64 * WGC * WGP), 0, s, a);
   return hipGetLastError();
 }
 
-template <int TC, int TP, int WGC, int WGP, int STAGES, int MINB, bool RB2 = false>
+template <int TC, int TP, int WGC, int WGP, int STAGES, int MINB, bool RB2 = false, typename T = bf16_t>
 static hipError_t conv_dma_go(const ConvArgs& a, hipStream_t s) {
-  if (hipError_t e = conv_dma_launch<TC, TP, WGC, WGP, STAGES, MINB, RB2>(a, s)) return e;
+  if (hipError_t e = conv_dma_launch<TC, TP, WGC, WGP, STAGES, MINB, RB2, T>(a, s)) return e;
   if (a.ksplit > 1) {
     const int64_t units = (int64_t)a.F * a.B * a.Ho * a.Wo * (a.Cout / 8);
     hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, s, a);
@@ -1769,6 +1793,14 @@ hipError_t launch_conv(const ConvArgs& a, int dtype, int tile, hipStream_t s) {
     if (tile == kTile256x128) return conv_go<bf16_t, 256, 128>(a, s);
     return conv_go<bf16_t, 128, 128>(a, s);
   }
+  // fp32 on the direct-to-LDS tiles (16 channels per K step; no split K, no staging epilogue)
+  if (tile == kTileDma256x128) return conv_dma_go<256, 128, 2, 2, 3, 2, false, float>(a, s);
+  if (tile == kTileDma256x256) return conv_dma_go<256, 256, 2, 2, 4, 1, true, float>(a, s);
+  if (tile == kTileDma128x256) return conv_dma_go<128, 256, 2, 2, 3, 2, false, float>(a, s);
+  if (tile == kTileDma128x128) return conv_dma_go<128, 128, 2, 2, 4, 2, false, float>(a, s);
+  if (tile == kTileDma16x256) return conv_dma_go<16, 256, 1, 4, 4, 2, false, float>(a, s);
+  if (tile == kTileDma256x256w8) return conv_dma_go<256, 256, 2, 4, 4, 1, false, float>(a, s);
+  if (tile == kTileDma256x256w8b) return conv_dma_go<256, 256, 4, 2, 4, 1, false, float>(a, s);
   if (tile == kTile32x256) return conv_go<float, 32, 256>(a, s);
   return conv_go<float, 128, 128>(a, s);
 }

@@ -352,8 +352,15 @@ static int pick_tile(const ConvArgs& a, int dtype) {
     if (forced == kTileDma16x256) return forced;
     return halo16 && a.Ho >= 32 && a.Wo >= 64 ? kTileHalo16x16x32 : kTileDma16x256;
   }
-  const bool dma_ok = dtype == kBF16 && a.mode != kEpiVideo && Cout % 8 == 0 && Cout > 64;
+  const bool dma_ok = a.mode != kEpiVideo && Cout % 8 == 0 && Cout > 64;
   if (!dma_ok) return Cout <= 64 ? kTile32x256 : kTile128x128;
+  if (dtype != kBF16) {
+    // fp32 on the direct-to-LDS tiles (no halo kernel, no split K): 128 x 256 with two
+    // workgroups per CU (faster on every decoder shape than the 256 x 256 tiles, whose
+    // fp32 fragments leave one wave per SIMD), 128 x 128 for the small level-0 frames
+    if (forced >= kTileDma256x128 && forced <= kTileDma256x256w8b) return forced;
+    return M < 16384 ? kTileDma128x128 : kTileDma128x256;
+  }
   const bool halo = conv_halo_supported(a, dtype, kTileHalo128x16x32);
   const bool forced_halo = forced == kTileHalo128x16x32 || forced == kTileHalo128x16x16;
   if (forced >= 0 && forced != kTileHalo16x16x32 && (!forced_halo || halo)) return forced;
