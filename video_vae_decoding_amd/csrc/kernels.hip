@@ -1424,7 +1424,10 @@ __global__ void __launch_bounds__(256) k_norm_v(const NormArgs a) {
 // the full scores and accumulates O^T += V^T P for its own dims. S^T's accumulator layout
 // (keys 4g..4g+3 of each 16-key tile in lane group g, one query per lane) is directly the
 // k layout of P as the B operand of the PV MFMA; V^T is read with the same key order.
-template <typename T, int NW, int DW>
+// PF: loads run one phase ahead of their use (8 waves, one workgroup per CU); without it
+// each block's K and V fragments are loaded right before their products, which suits the
+// 4-wave variants, two workgroups of which share a CU.
+template <typename T, int NW, int DW, bool PF = (NW >= 8)>
 __global__ void __launch_bounds__(64 * NW) k_attn(const AttnArgs a) {
   using X = Elem<T>;
   constexpr bool BF = sizeof(T) == 2;
@@ -1460,8 +1463,34 @@ __global__ void __launch_bounds__(64 * NW) k_attn(const AttnArgs a) {
   for (int dt = 0; dt < NDT; ++dt) o[dt][0] = o[dt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
 
+  // PF: a block's K fragments are loaded during the block before (behind its reduction,
+  // softmax and P V products), and its V fragments (bf16) at the top of the block, ahead
+  // of the S products.
+  uint4 kf[NKS][2];
+  auto load_k = [&](int kv0) {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const int key = min(kv0 + kt * 16 + l16, S - 1);
+        kf[ks][kt] = *(const uint4*)(K + (int64_t)key * C + dw0 + ks * KS + g * (BF ? 8 : 4));
+      }
+  };
+  if (PF && kb0 < kb1) load_k(kb0 * 32);
+
   int par = 0;
   for (int kv0 = kb0 * 32; kv0 < kb1 * 32; kv0 += 32, par ^= 1) {
+    uint4 vf[BF ? NDT : 1];
+    auto load_v = [&]() {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const T* vrow = Vt + (int64_t)(dw0 + dt * 16 + l16) * Sp + kv0 + 4 * g;
+        const uint2 lo = *(const uint2*)vrow, hi = *(const uint2*)(vrow + 16);
+        vf[dt] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
+    };
+    if constexpr (BF && PF) load_v();
+    if constexpr (!PF) load_k(kv0);
     f32x4_t s[2][2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) s[kt][0] = s[kt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -1469,12 +1498,13 @@ __global__ void __launch_bounds__(64 * NW) k_attn(const AttnArgs a) {
     for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        const int key = min(kv0 + kt * 16 + l16, S - 1);
-        const uint4 kf = *(const uint4*)(K + (int64_t)key * C + dw0 + ks * KS + g * (BF ? 8 : 4));
-        Mma<T>::run(s[kt][0], kf, qf[ks][0]);
-        Mma<T>::run(s[kt][1], kf, qf[ks][1]);
+        Mma<T>::run(s[kt][0], kf[ks][kt], qf[ks][0]);
+        Mma<T>::run(s[kt][1], kf[ks][kt], qf[ks][1]);
       }
     }
+    // (after the last block this loads keys it will not use: kept unconditional, so that the
+    // load counts the waits below see are the same on every iteration)
+    if constexpr (PF) load_k(kv0 + 32);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -1547,13 +1577,11 @@ __global__ void __launch_bounds__(64 * NW) k_attn(const AttnArgs a) {
         pb[qt].z = pack2_bf16(p[1][qt][0], p[1][qt][1]);
         pb[qt].w = pack2_bf16(p[1][qt][2], p[1][qt][3]);
       }
+      if constexpr (!PF) load_v();
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const T* vrow = Vt + (int64_t)(dw0 + dt * 16 + l16) * Sp + kv0 + 4 * g;
-        const uint2 lo = *(const uint2*)vrow, hi = *(const uint2*)(vrow + 16);
-        const uint4 vf = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        Mma<T>::run(o[dt][0], vf, pb[0]);
-        Mma<T>::run(o[dt][1], vf, pb[1]);
+        Mma<T>::run(o[dt][0], vf[dt], pb[0]);
+        Mma<T>::run(o[dt][1], vf[dt], pb[1]);
       }
     } else {
 #pragma unroll
