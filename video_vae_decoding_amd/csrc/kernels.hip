@@ -111,6 +111,14 @@ struct Mma<float> {
 // ------------------------------------------------------------------ conv epilogue
 
 // v[0..3]: accumulated sums + bias for output channels c..c+3 at (frame t, batch b, y, x).
+// Slot of key pix in a frame's row of V^T: within each block of 32 keys, key 16 kt + 4 g + e
+// (kt < 2, g < 4, e < 4) sits at 8 g + 4 kt + e. One lane of the attention's P V product
+// takes keys 4g..4g+3 of both 16-key halves of a block, which are then one 16-byte vector.
+__device__ __forceinline__ int vt_slot(int pix) {
+  const int r = pix & 31;
+  return (pix & ~31) | ((r & 12) << 1) | ((r & 16) >> 2) | (r & 3);
+}
+
 template <typename T>
 __device__ __forceinline__ void conv_epilogue(const ConvArgs& a, int t, int b, int y, int x, int c, float v[4]) {
   using X = Elem<T>;
@@ -156,7 +164,7 @@ __device__ __forceinline__ void conv_epilogue(const ConvArgs& a, int t, int b, i
       T* o = (T*)(c < C ? a.q : a.k) + ((int64_t)fr * a.S + pix) * C + (c < C ? c : c - C);
       X::st4(o, v);
     } else {
-      T* o = (T*)a.vt + ((int64_t)fr * C + (c - 2 * C)) * a.Sp + pix;
+      T* o = (T*)a.vt + ((int64_t)fr * C + (c - 2 * C)) * a.Sp + vt_slot(pix);
 #pragma unroll
       for (int e = 0; e < 4; ++e) X::st(o + (int64_t)e * a.Sp, v[e]);
     }
@@ -419,7 +427,7 @@ __device__ __forceinline__ void epilogue8_bf16(const ConvArgs& a, int t, int b, 
     if (c < 2 * C) {
       *(uint4*)((T*)(c < C ? a.q : a.k) + ((int64_t)fr * a.S + pix) * C + (c < C ? c : c - C)) = pack8_bf16(v);
     } else {
-      T* o = (T*)a.vt + ((int64_t)fr * C + (c - 2 * C)) * a.Sp + pix;
+      T* o = (T*)a.vt + ((int64_t)fr * C + (c - 2 * C)) * a.Sp + vt_slot(pix);
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[(int64_t)e * a.Sp].u = f2bf(v[e]);
     }
@@ -1423,7 +1431,8 @@ __global__ void __launch_bounds__(256) k_norm_v(const NormArgs a) {
 // then every wave reads the whole sum), then every wave runs the online softmax on
 // the full scores and accumulates O^T += V^T P for its own dims. S^T's accumulator layout
 // (keys 4g..4g+3 of each 16-key tile in lane group g, one query per lane) is directly the
-// k layout of P as the B operand of the PV MFMA; V^T is read with the same key order.
+// k layout of P as the B operand of the PV MFMA; V^T is stored with its keys in that order
+// (vt_slot), so a lane's 8 keys of a block are one 16-byte load.
 // PF: loads run one phase ahead of their use (8 waves, one workgroup per CU); without it
 // each block's K and V fragments are loaded right before their products, which suits the
 // 4-wave variants, two workgroups of which share a CU.
@@ -1439,9 +1448,15 @@ __global__ void __launch_bounds__(64 * NW) k_attn(const AttnArgs a) {
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int l16 = lane & 15, g = lane >> 4;
-  const int fr = blockIdx.y, q0 = blockIdx.x * 32;
+  // (query block, frame, key range), query blocks fastest, renumbered so that each XCD runs
+  // a contiguous run: its CUs sweep the same frame's (or key range's) K and V together,
+  // which its L2 then serves to all of them
+  const int L = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int N = xcd_remap(L, gridDim.x * gridDim.y * gridDim.z);
+  const int qb = N % gridDim.x, fz = N / gridDim.x;
+  const int fr = fz % gridDim.y, q0 = qb * 32;
   // key range of this workgroup: blocks of 32 keys [kb0, kb1) of the frame's ceil(S / 32)
-  const int nkb = (a.S + 31) / 32, kz = blockIdx.z;
+  const int nkb = (a.S + 31) / 32, kz = fz / gridDim.y;
   const int kb0 = (int)((int64_t)nkb * kz / a.ksplit), kb1 = (int)((int64_t)nkb * (kz + 1) / a.ksplit);
   const int C = a.C, S = a.S, Sp = a.Sp;
   const T* Q = (const T*)a.q + (int64_t)fr * S * C;
@@ -1484,9 +1499,8 @@ __global__ void __launch_bounds__(64 * NW) k_attn(const AttnArgs a) {
     auto load_v = [&]() {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const T* vrow = Vt + (int64_t)(dw0 + dt * 16 + l16) * Sp + kv0 + 4 * g;
-        const uint2 lo = *(const uint2*)vrow, hi = *(const uint2*)(vrow + 16);
-        vf[dt] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        // keys 4g..4g+3 of both halves of the block: one vector (vt_slot)
+        vf[dt] = *(const uint4*)(Vt + (int64_t)(dw0 + dt * 16 + l16) * Sp + kv0 + 8 * g);
       }
     };
     if constexpr (BF && PF) load_v();
@@ -1586,10 +1600,10 @@ __global__ void __launch_bounds__(64 * NW) k_attn(const AttnArgs a) {
     } else {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const T* vrow = Vt + (int64_t)(dw0 + dt * 16 + l16) * Sp + kv0 + 4 * g;
+        const T* vrow = Vt + (int64_t)(dw0 + dt * 16 + l16) * Sp + kv0 + 8 * g;  // (vt_slot)
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
-          const float4 vf = *(const float4*)(vrow + kt * 16);
+          const float4 vf = *(const float4*)(vrow + kt * 4);
           const float vv[4] = {vf.x, vf.y, vf.z, vf.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
