@@ -1424,6 +1424,25 @@ __global__ void __launch_bounds__(256) k_norm_v(const NormArgs a) {
 
 // ------------------------------------------------------------------ attention
 //
+// Max or sum over each aligned group of N (2, 4, 8 or 16) lanes, every lane getting the
+// group's result, with DPP lane moves (no LDS): swaps within pairs and quads, then the
+// mirror of each half-row (8 lanes) and of each row (16 lanes). The partners' values are
+// combined in one order for the whole group, so every lane holds the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <int N, bool MAX>
+__device__ __forceinline__ float group_reduce(float v) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "group of 1 to 16 lanes");
+  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+  if constexpr (N >= 2) v = op(v, dpp_mov<0xB1>(v));   // quad_perm [1, 0, 3, 2]
+  if constexpr (N >= 4) v = op(v, dpp_mov<0x4E>(v));   // quad_perm [2, 3, 0, 1]
+  if constexpr (N >= 8) v = op(v, dpp_mov<0x141>(v));  // row_half_mirror
+  if constexpr (N >= 16) v = op(v, dpp_mov<0x140>(v)); // row_mirror
+  return v;
+}
+//
 // One workgroup: 32 queries (2 tiles of 16) of one frame, NW waves; wave w owns head dims
 // [w*DW, (w+1)*DW). Per block of 32 keys each wave computes its partial S^T = K Q^T over its
 // dims (MFMA, Q fragments held in registers), the partials are summed through LDS (each
@@ -1433,18 +1452,31 @@ __global__ void __launch_bounds__(256) k_norm_v(const NormArgs a) {
 // (keys 4g..4g+3 of each 16-key tile in lane group g, one query per lane) is directly the
 // k layout of P as the B operand of the PV MFMA; V^T is stored with its keys in that order
 // (vt_slot), so a lane's 8 keys of a block are one 16-byte load.
-// PF: loads run one phase ahead of their use (8 waves, one workgroup per CU); without it
-// each block's K and V fragments are loaded right before their products, which suits the
-// 4-wave variants, two workgroups of which share a CU.
-template <typename T, int NW, int DW, bool PF = (NW >= 8)>
+// PF: loads run one phase ahead of their use (bf16 with 8 waves, one workgroup per CU);
+// without it each block's K and V fragments are loaded right before their products, which
+// suits the 4-wave variants, two workgroups of which share a CU, and leaves the fp32
+// variant with C = 1024 the registers it needs without spills.
+// RS (8 waves): the summed scores are scattered over the waves and every wave then runs the
+// online softmax over the whole tile for itself, after the second barrier, where it
+// overlaps the other waves' products. Without RS (fewer waves) each wave finishes the
+// softmax of its own query rows and shares P and the rescale factors through LDS.
+template <typename T, int NW, int DW, bool PF = (NW >= 8 && sizeof(T) == 2), bool RS = (NW >= 8)>
 __global__ void __launch_bounds__(64 * NW) k_attn(const AttnArgs a) {
   using X = Elem<T>;
   constexpr bool BF = sizeof(T) == 2;
   constexpr int KS = BF ? 32 : 16;  // head dims per S MFMA step
   constexpr int NKS = DW / KS;
   constexpr int NDT = DW / 16;       // 16-dim tiles of O per wave
+  // softmax rows: wave w finishes queries [w * QPW, (w + 1) * QPW) of the block, LPQ lanes
+  // per query, EPL consecutive keys per lane
+  constexpr int QPW = 32 / NW, LPQ = 64 / QPW, EPL = 32 / LPQ;
+  static_assert(QPW * NW == 32 && LPQ * QPW == 64 && EPL * LPQ == 32, "the tile splits evenly over the lanes");
+  constexpr int PR = BF ? 40 : 36;  // P row stride in elements (16-byte aligned, padded)
   __shared__ f32x4_t red[2][NW][4][64];  // each wave's partial S^T tile (1,024 floats)
-  __shared__ f32x4_t rsum[2][4][64];     // the summed tile
+  __shared__ f32x4_t rsum[2][RS ? 4 : 1][64];  // (RS) the summed tile
+  __shared__ __attribute__((aligned(16))) T ptile[2][RS ? 1 : 32][PR];  // P (rounded to T), keys in vt_slot order
+  __shared__ float alph[2][RS ? 1 : 32];  // each query's rescale factor of the block
+  __shared__ float2 mlq[RS ? 1 : 32];     // each query's final (max, sum)
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int l16 = lane & 15, g = lane >> 4;
@@ -1476,7 +1508,11 @@ __global__ void __launch_bounds__(64 * NW) k_attn(const AttnArgs a) {
   f32x4_t o[NDT][2];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) o[dt][0] = o[dt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
+  // the softmax row this lane finishes: query sq of the block (tile sqt, row sql), keys
+  // k0 .. k0 + EPL - 1 of each key block; its running max and sum (the same in the LPQ lanes)
+  const int sq = w * QPW + lane / LPQ, sqt = sq >> 4, sql = sq & 15, k0 = (lane % LPQ) * EPL;
+  float mrow = -INFINITY, lrow = 0.f;
+  float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};  // (RS) per query tile
 
   // PF: a block's K fragments are loaded during the block before (behind its reduction,
   // softmax and P V products), and its V fragments (bf16) at the top of the block, ahead
@@ -1524,72 +1560,133 @@ __global__ void __launch_bounds__(64 * NW) k_attn(const AttnArgs a) {
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) red[par][w][kt * 2 + qt][lane] = s[kt][qt];
     __syncthreads();
-    {
-      // reduce-scatter: wave w sums floats [w * FPW, (w + 1) * FPW) of the tile over the waves,
-      // in wave order, and every wave then reads the whole summed tile
-      constexpr int FPW = 1024 / NW, FPL = FPW / 64;
-      static_assert(FPL * 64 * NW == 1024, "the tile splits evenly over the waves' lanes");
-      const float* rf = (const float*)&red[par][0][0][0];
-      float* sf = (float*)&rsum[par][0][0];
-      const int f0 = w * FPW + lane * FPL;
-      float acc[FPL];
+    float p[2][2][4];  // (RS, or fp32) key 16 kt + 4 g + e of query 16 qt + l16
+    if constexpr (RS) {
+      {
+        // reduce-scatter: wave w sums floats [w * FPW, (w + 1) * FPW) of the tile over the waves,
+        // in wave order, and every wave then reads the whole summed tile
+        constexpr int FPW = 1024 / NW, FPL = FPW / 64;
+        static_assert(FPL * 64 * NW == 1024, "the tile splits evenly over the waves' lanes");
+        const float* rf = (const float*)&red[par][0][0][0];
+        float* sf = (float*)&rsum[par][0][0];
+        const int f0 = w * FPW + lane * FPL;
+        float acc[FPL];
 #pragma unroll
-      for (int e = 0; e < FPL; ++e) acc[e] = rf[f0 + e];
+        for (int e = 0; e < FPL; ++e) acc[e] = rf[f0 + e];
 #pragma unroll
-      for (int ww = 1; ww < NW; ++ww)
+        for (int ww = 1; ww < NW; ++ww)
 #pragma unroll
-        for (int e = 0; e < FPL; ++e) acc[e] += rf[ww * 1024 + f0 + e];
+          for (int e = 0; e < FPL; ++e) acc[e] += rf[ww * 1024 + f0 + e];
 #pragma unroll
-      for (int e = 0; e < FPL; ++e) sf[f0 + e] = acc[e];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) s[kt][qt] = rsum[par][kt * 2 + qt][lane];
-    // online softmax; key of element e in tile kt: kv0 + kt*16 + 4g + e
-    float p[2][2][4];
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      float mx = -INFINITY;
+        for (int e = 0; e < FPL; ++e) sf[f0 + e] = acc[e];
+      }
+      __syncthreads();
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int key = kv0 + kt * 16 + 4 * g + e;
-          const float v = key < S ? s[kt][qt][e] * sc : -INFINITY;
-          p[kt][qt][e] = v;
-          mx = fmaxf(mx, v);
+        for (int qt = 0; qt < 2; ++qt) s[kt][qt] = rsum[par][kt * 2 + qt][lane];
+      // online softmax; key of element e in tile kt: kv0 + kt*16 + 4g + e
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int key = kv0 + kt * 16 + 4 * g + e;
+            const float v = key < S ? s[kt][qt][e] * sc : -INFINITY;
+            p[kt][qt][e] = v;
+            mx = fmaxf(mx, v);
+          }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mnew = fmaxf(mrun[qt], mx);
+        const float alpha = exp2f(mrun[qt] - mnew);
+        float sum = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float pe = exp2f(p[kt][qt][e] - mnew);
+            p[kt][qt][e] = pe;
+            sum += pe;
+          }
+        sum += __shfl_xor(sum, 16, 64);
+        sum += __shfl_xor(sum, 32, 64);
+        lrun[qt] = lrun[qt] * alpha + sum;
+        mrun[qt] = mnew;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[dt][qt] *= alpha;
+      }
+    } else {
+      {
+        // each lane sums its EPL scores over the waves' partials, in wave order (deterministic),
+        // then the online softmax of its query runs over the query's LPQ lanes; P goes to LDS
+        // rounded to T, with the query's rescale factor. Element (key 16 kt + 4 g + e, query
+        // 16 qt + l) of a partial is float 4 (64 (2 kt + qt) + l + 16 g) + e.
+        const float* rf = (const float*)&red[par][0][0][0];
+        float v[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          const int key = k0 + e;
+          const int idx = ((((key >> 4) * 2 + sqt) * 64 + sql + 16 * ((key >> 2) & 3)) << 2) + (key & 3);
+          float acc = rf[idx];
+#pragma unroll
+          for (int ww = 1; ww < NW; ++ww) acc += rf[ww * 1024 + idx];
+          v[e] = kv0 + key < S ? acc * sc : -INFINITY;
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mnew = fmaxf(mrun[qt], mx);
-      const float alpha = exp2f(mrun[qt] - mnew);
-      float sum = 0.f;
+        float mx = v[0];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+        for (int e = 1; e < EPL; ++e) mx = fmaxf(mx, v[e]);
+        mx = group_reduce<LPQ, true>(mx);
+        const float mnew = fmaxf(mrow, mx);
+        const float alpha = exp2f(mrow - mnew);
+        float sum = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float pe = exp2f(p[kt][qt][e] - mnew);
-          p[kt][qt][e] = pe;
-          sum += pe;
+        for (int e = 0; e < EPL; ++e) {
+          v[e] = exp2f(v[e] - mnew);
+          sum += v[e];
         }
-      sum += __shfl_xor(sum, 16, 64);
-      sum += __shfl_xor(sum, 32, 64);
-      lrun[qt] = lrun[qt] * alpha + sum;
-      mrun[qt] = mnew;
+        sum = group_reduce<LPQ, false>(sum);
+        lrow = lrow * alpha + sum;
+        mrow = mnew;
+        T* prow = &ptile[par][sq][0];
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) o[dt][qt] *= alpha;
+        for (int e = 0; e < EPL; ++e) X::st(prow + vt_slot(k0 + e), v[e]);
+        if (lane % LPQ == 0) alph[par][sq] = alpha;
+      }
+      __syncthreads();
+      // O^T[d][q] = alpha_q O^T[d][q] + V^T[d][key] P^T[key][q]; this lane's column is query
+      // 16 qt + l16
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        const float al = alph[par][qt * 16 + l16];
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[dt][qt] *= al;
+      }
+      if constexpr (!BF) {
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) {
+            const float4 pv = *(const float4*)&ptile[par][qt * 16 + l16][8 * g + 4 * kt];
+            p[kt][qt][0] = pv.x, p[kt][qt][1] = pv.y, p[kt][qt][2] = pv.z, p[kt][qt][3] = pv.w;
+          }
+      }
     }
-    // O^T[d][q] += V^T[d][key] P^T[key][q]
     if constexpr (BF) {
+      // P^T's B fragment: keys 4g..4g+3 of both 16-key halves, one vector (vt_slot)
       uint4 pb[2];
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
-        pb[qt].x = pack2_bf16(p[0][qt][0], p[0][qt][1]);
-        pb[qt].y = pack2_bf16(p[0][qt][2], p[0][qt][3]);
-        pb[qt].z = pack2_bf16(p[1][qt][0], p[1][qt][1]);
-        pb[qt].w = pack2_bf16(p[1][qt][2], p[1][qt][3]);
+        if constexpr (RS) {
+          pb[qt].x = pack2_bf16(p[0][qt][0], p[0][qt][1]);
+          pb[qt].y = pack2_bf16(p[0][qt][2], p[0][qt][3]);
+          pb[qt].z = pack2_bf16(p[1][qt][0], p[1][qt][1]);
+          pb[qt].w = pack2_bf16(p[1][qt][2], p[1][qt][3]);
+        } else {
+          pb[qt] = *(const uint4*)&ptile[par][qt * 16 + l16][8 * g];
+        }
       }
       if constexpr (!PF) load_v();
 #pragma unroll
@@ -1612,6 +1709,16 @@ __global__ void __launch_bounds__(64 * NW) k_attn(const AttnArgs a) {
           }
         }
       }
+    }
+  }
+  if constexpr (!RS) {
+    // every wave's queries' final (max, sum)
+    if (lane % LPQ == 0) mlq[sq] = make_float2(mrow, lrow);
+    __syncthreads();
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const float2 ml = mlq[qt * 16 + l16];
+      mrun[qt] = ml.x, lrun[qt] = ml.y;
     }
   }
   if (a.ksplit > 1) {
