@@ -61,6 +61,7 @@ def compare(got, x, ws, mode, what):
 @pytest.mark.parametrize("layout", ["ncthw", "nthwc"])
 @pytest.mark.parametrize("C,T,h,w,B,peaked", [(64, 3, 4, 5, 2, False), (64, 2, 6, 9, 1, True),
                                                (128, 2, 7, 11, 1, False), (256, 1, 9, 8, 1, True),
+                                               (384, 1, 7, 9, 1, False), (512, 2, 6, 7, 1, True),
                                                (1024, 2, 5, 13, 1, False)])
 def test_attn_small(C, T, h, w, B, peaked, layout, mode):
     say("attn", C, T, h, w, B, peaked, layout, mode)
