@@ -1166,13 +1166,17 @@ __global__ void __launch_bounds__(64 * WGC * WGP, 1) k_conv_halo(const ConvArgs 
           __builtin_amdgcn_sched_barrier(0);
           read_frags(set ^ 1, wb[jn], j == 8 ? pnext : pcur, jn);
           mfma_all(set);
-          // one LDS read between groups of MFMAs
-          constexpr int MPR = (TCN * TPN + TCN + TPN - 1) / (TCN + TPN);
+          // one LDS read between groups of MFMAs, the reads early in the step (two MFMAs each,
+          // the rest after them) so that they have landed by its end: 1-3% faster than spread
+          // over the whole step, and 3% faster than all reads first
+          constexpr int NRD = TCN + TPN, NMF = TCN * TPN;
+          constexpr int MPR = NMF >= 2 * NRD ? 2 : (NMF + NRD - 1) / NRD;
 #pragma unroll
-          for (int r = 0; r < TCN + TPN; ++r) {
+          for (int r = 0; r < NRD; ++r) {
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, MPR, 0);
           }
+          if constexpr (NMF > MPR * NRD) __builtin_amdgcn_sched_group_barrier(0x008, NMF - MPR * NRD, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
         // the cursors move one group on
