@@ -155,7 +155,7 @@ int wanvae_profile_read(int kind, double *ms, int64_t *launches, double *flops, 
  * Conv kernel selection, for testing and tuning. By default (kernel = -1) each conv takes the
  * kernel its shape and dtype call for. kernel in 0..WANVAE_CONV_KERNELS-1 asks every later
  * conv of any thread to use that kernel where it can run the conv (bf16 only for kernels 2
- * and 10..12; kernels 10 and 12 only for 3x3 spatial convs with
+ * and 10..13; kernels 10, 12 and 13 only for 3x3 spatial convs with
  * Cin % 32 == 0 and Cout % 128 == 0, kernel 11 only for conv_out); other convs
  * keep the default. The kernels compute the same sums in different orders, so results agree
  * to rounding, not bit for bit. The environment variable WANVAE_CONV_TILE gives the initial
@@ -166,8 +166,9 @@ int wanvae_profile_read(int kind, double *ms, int64_t *launches, double *flops, 
  *  10: 3x3 halo tile, 128 channels x 16 x 32 positions, input patch shared by the taps (bf16)
  *  11: the same with 16 channels, for conv_out's unpatchify + clamp store (bf16)
  *  12: the 128-channel halo tile on 16 x 16 blocks (bf16)
+ *  13: the 128-channel halo tile on 32 x 16 blocks (bf16)
  */
-#define WANVAE_CONV_KERNELS 13
+#define WANVAE_CONV_KERNELS 14
 int wanvae_set_conv_kernel(int kernel);
 
 /*

@@ -81,7 +81,7 @@ def small32():
     return z, W, want, noise
 
 
-@pytest.mark.parametrize("kernel", [-1, 10, 12, 9, 5, 3])
+@pytest.mark.parametrize("kernel", [-1, 10, 12, 13, 9, 5, 3])
 def test_small32_bf16_decode_each_conv_kernel(small32, conv_kernel, kernel):
     """decoder_base_dim 32: every 3x3 conv of the 128-channel levels, the upsampling ones
     included, runs on the forced kernel (10: the halo tile) with the residual and DupUp3D

@@ -93,6 +93,7 @@ enum ConvTile {
   kTileHalo128x16x32 = 10, // bf16 3x3 convs: 128 channels x a 16 x 32 block, input patch reused over the taps
   kTileHalo16x16x32 = 11,  // the same for conv_out (up to 16 channels, the video store)
   kTileHalo128x16x16 = 12, // 128 channels x a 16 x 16 block (small frames, with split K)
+  kTileHalo128x32x16 = 13, // 128 channels x a 32 x 16 block (frames that 16-column blocks pad less)
 };
 
 // One tile of the tiled decode (tiles.hip): the decoded tile cur [planes][H][W] (planes = batch x

@@ -1930,6 +1930,10 @@ hipError_t launch_conv(const ConvArgs& a, int dtype, int tile, hipStream_t s) {
     if (!conv_halo_supported(a, dtype, tile)) return hipErrorInvalidValue;
     return conv_halo_go<16, 16, 32, 1, 8>(a, s);
   }
+  if (tile == kTileHalo128x32x16) {
+    if (!conv_halo_supported(a, dtype, tile)) return hipErrorInvalidValue;
+    return conv_halo_go<128, 32, 16, 2, 4>(a, s);
+  }
   if (tile == kTileHalo128x16x16) {
     if (!conv_halo_supported(a, dtype, tile)) return hipErrorInvalidValue;
     return conv_halo_go<128, 16, 16, 2, 4>(a, s);

@@ -362,14 +362,20 @@ static int pick_tile(const ConvArgs& a, int dtype) {
     return M < 16384 ? kTileDma128x128 : kTileDma128x256;
   }
   const bool halo = conv_halo_supported(a, dtype, kTileHalo128x16x32);
-  const bool forced_halo = forced == kTileHalo128x16x32 || forced == kTileHalo128x16x16;
+  const bool forced_halo = forced == kTileHalo128x16x32 || forced == kTileHalo128x16x16 || forced == kTileHalo128x32x16;
   if (forced >= 0 && forced != kTileHalo16x16x32 && (!forced_halo || halo)) return forced;
   // 3x3 convs on frames of at least 32 x 64: the halo tile (input patch shared by the nine
   // spatial taps), 16 x 32 blocks, or 16 x 16 blocks with split K where the frames leave
   // the chip short of blocks (the level-0 layers: 3,520 positions per frame); 256 x 256
   // tiles (8 waves of 64 x 128) for the other convs with enough positions to fill the chip;
   // 128 x 128 (with split K) for the rest
-  if (halo && a.Ho >= 32 && a.Wo >= 64) return M >= 16384 ? kTileHalo128x16x32 : kTileHalo128x16x16;
+  if (halo && a.Ho >= 32 && a.Wo >= 64) {
+    if (M < 16384) return kTileHalo128x16x16;
+    // 512-position blocks in the orientation that pads the frame less (16 x 32 on a tie):
+    // 32 x 16 for the 320 x 176 frames of a portrait video's level 2
+    auto up = [](int64_t v, int64_t m) { return (v + m - 1) / m * m; };
+    return up(a.Ho, 32) * up(a.Wo, 16) < up(a.Ho, 16) * up(a.Wo, 32) ? kTileHalo128x32x16 : kTileHalo128x16x32;
+  }
   if (M < 16384) return kTileDma128x128;
   return Cout % 256 == 0 ? kTileDma256x256w8b : kTileDma256x128;
 }
@@ -410,6 +416,7 @@ static int split_for(const ConvArgs& a, int tile, int dtype, const SplitBuf& sb)
     case kTileDma16x256: TC = 16, TP = 256; break;
     case kTileHalo128x16x32: TC = 128, TPY = 16, TPX = 32; break;
     case kTileHalo128x16x16: TC = 128, TPY = 16, TPX = 16; break;
+    case kTileHalo128x32x16: TC = 128, TPY = 32, TPX = 16; break;
     default: return 1;
   }
   if (dtype != kBF16 || a.mode == kEpiVideo || a.Cout % 8 || sb.p == nullptr) return 1;

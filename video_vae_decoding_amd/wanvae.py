@@ -247,7 +247,7 @@ def wanvae_attn_block(x: torch.Tensor, gamma, qkv_w, qkv_b, proj_w, proj_b, layo
 attn_block = wanvae_attn_block
 
 
-CONV_KERNELS = 13
+CONV_KERNELS = 14
 
 
 def wanvae_set_conv_kernel(kernel: int) -> None:
