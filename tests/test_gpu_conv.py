@@ -30,10 +30,12 @@ SMALL = [
 
 
 # bf16 convs the halo-tile kernel takes by default (3x3, Cin % 32 == 0, Cout % 128 == 0, frames
-# of at least 32 x 64, at least 16,384 positions): ragged 16 x 32 blocks, batch 2, a 2-D conv
+# of at least 32 x 64, at least 16,384 positions): ragged 16 x 32 blocks, batch 2, a 2-D conv,
+# and a 62 x 80 frame, which 32 x 16 blocks pad less than 16 x 32 ones (64 x 80 against 64 x 96)
 HALO = [
     (32, 128, 3, 3, 3, 2, 40, 210, 2, 2),
     (64, 256, 1, 3, 3, 1, 70, 120, 0, 2),
+    (32, 128, 3, 3, 3, 2, 62, 80, 2, 2),
 ]
 
 
