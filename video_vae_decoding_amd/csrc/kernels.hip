@@ -1478,7 +1478,12 @@ __global__ void __launch_bounds__(64 * NW) k_attn(const AttnArgs a) {
   constexpr int QPW = 32 / NW, LPQ = 64 / QPW, EPL = 32 / LPQ;
   static_assert(QPW * NW == 32 && LPQ * QPW == 64 && EPL * LPQ == 32, "the tile splits evenly over the lanes");
   constexpr int PR = BF ? 40 : 36;  // P row stride in elements (16-byte aligned, padded)
-  __shared__ f32x4_t red[2][NW][4][64];  // each wave's partial S^T tile (1,024 floats)
+  // each wave's partial S^T tile: 4 (kt, qt) tiles of 64 accumulator vectors, vector l16 + 16 g
+  // at slot l16 + GS g. With RS the tile is dense (the reduce-scatter reads it as 1,024 floats);
+  // without, key groups are 18 slots apart and (kt, qt) tiles 76, so that the 16 lanes of two
+  // queries' rows (8 (kt, g) each) fall in 16 different 4-bank groups
+  constexpr int GS = RS ? 16 : 18, TS = RS ? 64 : 76;
+  __shared__ f32x4_t red[2][NW][4][TS];
   __shared__ f32x4_t rsum[2][RS ? 4 : 1][64];  // (RS) the summed tile
   __shared__ __attribute__((aligned(16))) T ptile[2][RS ? 1 : 32][PR];  // P (rounded to T), keys in vt_slot order
   __shared__ float alph[2][RS ? 1 : 32];  // each query's rescale factor of the block
@@ -1564,7 +1569,7 @@ __global__ void __launch_bounds__(64 * NW) k_attn(const AttnArgs a) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) red[par][w][kt * 2 + qt][lane] = s[kt][qt];
+      for (int qt = 0; qt < 2; ++qt) red[par][w][kt * 2 + qt][l16 + GS * g] = s[kt][qt];
     __syncthreads();
     float p[2][2][4];  // (RS, or fp32) key 16 kt + 4 g + e of query 16 qt + l16
     if constexpr (RS) {
@@ -1629,16 +1634,16 @@ __global__ void __launch_bounds__(64 * NW) k_attn(const AttnArgs a) {
         // each lane sums its EPL scores over the waves' partials, in wave order (deterministic),
         // then the online softmax of its query runs over the query's LPQ lanes; P goes to LDS
         // rounded to T, with the query's rescale factor. Element (key 16 kt + 4 g + e, query
-        // 16 qt + l) of a partial is float 4 (64 (2 kt + qt) + l + 16 g) + e.
+        // 16 qt + l) of a partial is float 4 (TS (2 kt + qt) + l + GS g) + e.
         const float* rf = (const float*)&red[par][0][0][0];
         float v[EPL];
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
           const int key = k0 + e;
-          const int idx = ((((key >> 4) * 2 + sqt) * 64 + sql + 16 * ((key >> 2) & 3)) << 2) + (key & 3);
+          const int idx = ((((key >> 4) * 2 + sqt) * TS + sql + GS * ((key >> 2) & 3)) << 2) + (key & 3);
           float acc = rf[idx];
 #pragma unroll
-          for (int ww = 1; ww < NW; ++ww) acc += rf[ww * 1024 + idx];
+          for (int ww = 1; ww < NW; ++ww) acc += rf[ww * 16 * TS + idx];
           v[e] = kv0 + key < S ? acc * sc : -INFINITY;
         }
         float mx = v[0];
