@@ -1458,15 +1458,15 @@ __device__ __forceinline__ float group_reduce(float v) {
 // (keys 4g..4g+3 of each 16-key tile in lane group g, one query per lane) is directly the
 // k layout of P as the B operand of the PV MFMA; V^T is stored with its keys in that order
 // (vt_slot), so a lane's 8 keys of a block are one 16-byte load.
-// PF: loads run one phase ahead of their use (bf16 with 8 waves, one workgroup per CU);
-// without it each block's K and V fragments are loaded right before their products, which
-// suits the 4-wave variants, two workgroups of which share a CU, and leaves the fp32
-// variant with C = 1024 the registers it needs without spills.
+// PF: loads run one phase ahead of their use (bf16, where the registers still allow the
+// variant's workgroups per CU: 8 waves, or 4 waves of at most 96 dims); without it each
+// block's K and V fragments are loaded right before their products, which leaves the fp32
+// variant with C = 1024 and the 4-wave C = 512 one the registers they need.
 // RS (8 waves): the summed scores are scattered over the waves and every wave then runs the
 // online softmax over the whole tile for itself, after the second barrier, where it
 // overlaps the other waves' products. Without RS (fewer waves) each wave finishes the
 // softmax of its own query rows and shares P and the rescale factors through LDS.
-template <typename T, int NW, int DW, bool PF = (NW >= 8 && sizeof(T) == 2), bool RS = (NW >= 8)>
+template <typename T, int NW, int DW, bool PF = (sizeof(T) == 2 && (NW >= 8 || DW <= 96)), bool RS = (NW >= 8)>
 __global__ void __launch_bounds__(64 * NW) k_attn(const AttnArgs a) {
   using X = Elem<T>;
   constexpr bool BF = sizeof(T) == 2;
