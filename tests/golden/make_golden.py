@@ -6,12 +6,14 @@ only through the causal caches), so the oracle decodes the first K_CHUNKS latent
 each full-size workload and this script keeps the video at N_SAMPLES seeded positions. The
 videos of a batch are independent, so a batch element can be decoded on its own.
 
-    python tests/golden/make_golden.py [--out DIR] config:mode[:batch][:f32] ...
+    python tests/golden/make_golden.py [--out DIR] [--chunks K] config:mode[:batch][:f32] ...
 
 Outputs, per job: ``<config>_<mode>[_b<batch>].npy`` (float32 sampled values) and the same
 name with ``.json`` (recipe, oracle wall time, summary statistics). With ``f32`` the oracle
 sums in float32 instead of float64 (name suffix ``_accf32``): the same decode in another
 accumulation order, which bounds how much a bf16 decode moves with the order of its sums.
+``--chunks K`` decodes K latent frames (4K - 3 video frames); the landscape files use 4, so that
+two chunks run in the steady state, where every time conv has two frames of history.
 """
 from __future__ import annotations
 
@@ -26,7 +28,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(os.path.dirname(HERE))
 sys.path.insert(0, ROOT)
 
-K_CHUNKS = 2          # latent frames decoded -> 4*K_CHUNKS - 3 = 5 video frames
+K_CHUNKS = 2          # default latent frames decoded -> 4*K_CHUNKS - 3 = 5 video frames
 N_SAMPLES = 65536
 SAMPLE_SEED = 20251202
 
@@ -49,11 +51,11 @@ def golden_paths(config, mode, batch=None, out=HERE, acc="f64"):
     return base + ".npy", base + ".json"
 
 
-def make(config, mode, batch=None, out=HERE, acc="f64"):
+def make(config, mode, batch=None, out=HERE, acc="f64", chunks=K_CHUNKS):
     import oracle
     import synthetic
     cfg = synthetic.DECODE_CONFIGS[config]
-    z = cfg.latents()[:, :, :K_CHUNKS]
+    z = cfg.latents()[:, :, :chunks]
     if batch is not None:
         z = z[batch:batch + 1]
     z = np.ascontiguousarray(z)
@@ -75,7 +77,7 @@ def make(config, mode, batch=None, out=HERE, acc="f64"):
     npy, js = golden_paths(config, mode, batch, out, acc)
     np.save(npy, vals)
     meta = {
-        "config": config, "mode": mode, "batch": batch, "acc": acc, "latent_frames": K_CHUNKS,
+        "config": config, "mode": mode, "batch": batch, "acc": acc, "latent_frames": chunks,
         "video_shape": list(video.shape), "n_samples": N_SAMPLES, "sample_seed": SAMPLE_SEED,
         "oracle_seconds": round(wall, 1), "oracle_chunk_seconds": [round(t, 1) for t in times],
         "host_cores": len(os.sched_getaffinity(0)),
@@ -94,6 +96,10 @@ if __name__ == "__main__":
         out = args[1]
         os.makedirs(out, exist_ok=True)
         args = args[2:]
+    chunks = K_CHUNKS
+    if args[:1] == ["--chunks"]:
+        chunks = int(args[1])
+        args = args[2:]
     jobs = []
     for a in args or [f"{c}:{m}" for c, m in JOBS]:
         parts = a.split(":")
@@ -101,4 +107,4 @@ if __name__ == "__main__":
         parts = [p for p in parts if p != "f32"]
         jobs.append((parts[0], parts[1] if len(parts) > 1 else "bf16", int(parts[2]) if len(parts) > 2 else None, acc))
     for c, m, b, acc in jobs:
-        make(c, m, b, out, acc)
+        make(c, m, b, out, acc, chunks)
