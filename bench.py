@@ -20,7 +20,8 @@ bounded sample.
 --workload picks another of the measured configurations (default ti2v5b_landscape_bf16):
 ti2v5b_landscape_fp32, ti2v5b_portrait_bf16, ti2v5b_landscape_b2_bf16 (whole decodes, frames/s),
 ti2v5b_landscape_bf16_tiled (the spatially tiled decode, tile 256 / stride 192 video pixels),
-conv1024_l0_bf16, conv256_l3_bf16 (one causal conv, TFLOP/s), attn1024_31f_bf16 (the attention
+conv1024_l0_bf16, conv256_l3_bf16 (one causal conv, TFLOP/s; the _yf32 variants store the float32
+sums unrounded), attn1024_31f_bf16 (the attention
 block over 31 frames, TFLOP/s), attn384_s14400_21f_bf16 and attn1024_s14400_21f_bf16 (the block
 over 21 frames of the Wan2.1 720p latent, 90x160 positions, at widths 384 and 1024).
 """
@@ -48,22 +49,57 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(cfg, W, mode="bf16"):
-    """The CPU oracle (as it stands: float64 sums, the mode's rounding points) decoding the
-    first latent frame of the same decoder on a crop of the latent with 1/16 of the frame area
-    (1/16 of a video frame's work, attention aside), scaled to full frames/s."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _blas():
+    """The BLAS libraries behind the oracle's products (torch.mm for the convs, numpy for the
+    attention) and their thread counts."""
+    import torch
+    cfg = torch.__config__.show()
+    tb = [l.strip() for l in cfg.splitlines() if "BLAS_INFO" in l or "LAPACK_INFO" in l]
+    try:
+        info = np.show_config(mode="dicts")
+        nb = info.get("Build Dependencies", {}).get("blas", {}).get("name", "unknown")
+    except Exception:  # noqa: BLE001
+        nb = "unknown"
+    return {"torch": "; ".join(tb) or "unknown", "torch_threads": torch.get_num_threads(), "numpy": nb}
+
+
+def cpu_baseline(cfg, W, mode="bf16", chunks=3):
+    """The CPU oracle as it stands (float64 sums, the mode's rounding points) decoding a causal
+    prefix of the workload: latent frames 0..chunks-1 (chunk 0, chunk 1, and steady-state chunks
+    with two frames of history) of batch element 0, on a crop of the latent with 1/16 of the frame
+    area. Measured: each chunk's seconds. Extrapolated, and labelled so: the full decode's time
+    as 16 x (t0 + t1 + (T - 2) x t_steady) (conv work scales with the area; the attention, which
+    scales with its square, is under 0.2% of the work) and its frames/s."""
     import oracle
     ch, cw = (11, 20) if cfg.h <= cfg.w else (20, 11)
-    z = cfg.latents()[:1, :, :1, :ch, :cw]
+    z = np.ascontiguousarray(cfg.latents()[:1, :, :chunks, :ch, :cw])
+    marks = []
     t0 = time.perf_counter()
-    v = oracle.decode(np.ascontiguousarray(z), W, mode)
-    dt = time.perf_counter() - t0
-    frac = (ch * cw) / (cfg.h * cfg.w)
-    return {"value": frac * v.shape[2] / dt, "unit": "frames/s", "cores": _cores(),
-            "kind": "oracle", "seconds": round(dt, 2),
-            "sample": f"oracle.decode ({mode} mode, float64 sums) of latent frame 0 on a {ch}x{cw} crop of the "
-                      f"[{cfg.B},48,{cfg.T},{cfg.h},{cfg.w}] latents (batch element 0): 1 video frame of "
-                      f"{16 * ch}x{16 * cw} = 1/16 of a {16 * cfg.h}x{16 * cfg.w} frame; value = (1/16 frame) / seconds"}
+    oracle.decode(z, W, mode, on_chunk=lambda i: marks.append(time.perf_counter()))
+    per = [b - a for a, b in zip([t0] + marks[:-1], marks)]
+    scale = (cfg.h * cfg.w) / (ch * cw)
+    t_full = scale * (per[0] + per[1] + (cfg.T - 2) * per[-1])
+    frames = cfg.B * cfg.frames
+    return {"value": round(frames / (cfg.B * t_full), 6), "unit": "frames/s", "cores": _cores(), "kind": "oracle",
+            "extrapolated": True, "seconds": round(sum(per), 2), "chunk_seconds": [round(t, 2) for t in per],
+            "full_decode_seconds_extrapolated": round(t_full, 1),
+            "cpu_model": _cpu_model(), "blas": _blas(),
+            "sample": f"oracle.decode ({mode} mode, float64 sums) of latent frames 0..{chunks - 1} (chunk 0, chunk 1 and "
+                      f"{chunks - 2} steady chunk) on a {ch}x{cw} crop of the [{cfg.B},48,{cfg.T},{cfg.h},{cfg.w}] latents "
+                      f"(batch element 0), 1/{scale:.0f} of the frame area; value = {frames} frames / the extrapolated "
+                      f"time of the whole batch, {cfg.B} x {scale:.0f} x (t0 + t1 + {cfg.T - 2} x t_steady) "
+                      "(extrapolated, not measured)"}
 
 
 CPU_SAMPLE_SECONDS = 10.0  # the single-op oracle samples repeat until this much CPU time has passed
@@ -153,6 +189,7 @@ DECODES = {"ti2v5b_landscape_bf16": ("ti2v5b_landscape", "bf16"), "ti2v5b_landsc
            "ti2v5b_landscape_bf16_tiled": ("ti2v5b_landscape", "bf16")}
 TILED = {"ti2v5b_landscape_bf16_tiled": ((256, 256), (192, 192))}  # the page's default tile and stride
 SINGLE = {"conv1024_l0_bf16": ("conv", "conv1024_l0"), "conv256_l3_bf16": ("conv", "conv256_l3"),
+          "conv1024_l0_bf16_yf32": ("conv", "conv1024_l0"), "conv256_l3_bf16_yf32": ("conv", "conv256_l3"),
           "attn1024_31f_bf16": ("attn", "attn1024_31f"), "attn384_s14400_21f_bf16": ("attn", "attn384_s14400_21f"),
           "attn1024_s14400_21f_bf16": ("attn", "attn1024_s14400_21f")}
 
@@ -187,12 +224,14 @@ def single_op(name, args):
         xt = torch.from_numpy(x).to(dev).to(bf).permute(0, 2, 3, 4, 1).contiguous()
         ct = torch.from_numpy(cache).to(dev).to(bf).permute(0, 2, 3, 4, 1).contiguous()
         wt, bt = torch.from_numpy(w).to(dev), torch.from_numpy(b).to(dev)
-        y = torch.empty(1, cfg.t, cfg.h, cfg.w, cfg.C, dtype=bf, device=dev)
-        ws = torch.empty(wanvae.conv_workspace_size(1, cfg.C, cfg.C, cfg.t, cfg.h, cfg.w, cfg.n_cache, "nthwc", bf),
+        ydt = torch.float32 if name.endswith("_yf32") else bf
+        y = torch.empty(1, cfg.t, cfg.h, cfg.w, cfg.C, dtype=ydt, device=dev)
+        ws = torch.empty(wanvae.conv_workspace_size(1, cfg.C, cfg.C, cfg.t, cfg.h, cfg.w, cfg.n_cache, "nthwc", bf, ydt),
                          dtype=torch.uint8, device=dev)
-        run = lambda: wanvae.wanvae_causal_conv3d(xt, ct, wt, bt, layout="nthwc", y=y, workspace=ws)
+        run = lambda: wanvae.wanvae_causal_conv3d(xt, ct, wt, bt, layout="nthwc", y=y, workspace=ws, y_dtype=ydt)
         flops = 2.0 * cfg.t * cfg.h * cfg.w * cfg.C * cfg.C * 27
-        config = {"workload": name, "x": [1, cfg.C, cfg.t, cfg.h, cfg.w], "n_cache": cfg.n_cache, "kernel": "3x3x3"}
+        config = {"workload": name, "x": [1, cfg.C, cfg.t, cfg.h, cfg.w], "n_cache": cfg.n_cache, "kernel": "3x3x3",
+                  "y_dtype": "fp32" if ydt == torch.float32 else "bf16"}
     else:
         cfg = synthetic.ATTN_CONFIGS[cfg_name]
         T = cfg.tensors()

@@ -80,7 +80,10 @@ typedef struct {
  *           WANVAE_ETOPOLOGY. Duplicate names -> WANVAE_EARG.
  *  video    output [B, 3, 4T-3, 16h, 16w] NCTHW of element type dtype, values in [-1, 1]
  *           (NaN propagates).
- *  Requires B >= 1, T >= 1, h >= 1, w >= 1, every width <= 1024 and a multiple of 8.
+ *  Requires B >= 1, T >= 1, h >= 1, w >= 1 and B * h * w <= 2^19. The decoder_base_dim b (the
+ *  input channels of conv_out) must be 16, 32, 64, 96, 128 or 256 (the mid-block width 4b is
+ *  one the attention kernels run: 64, 128, 256, 384, 512 or 1024), else WANVAE_ETOPOLOGY; this
+ *  is checked with the other arguments, before anything is launched.
  */
 int wanvae_decode_workspace_size(int64_t B, int64_t T, int64_t h, int64_t w,
                                  const wanvae_tensor *weights, int64_t n_weights,
@@ -94,23 +97,34 @@ int wanvae_decode(const void *z, int32_t z_dtype, int64_t B, int64_t T, int64_t 
  * of a chunk x with n_cache frames of history:
  *   y[b,o,t,y,x] = bias[o] + sum_{i,dt,dy,dx} W[o,i,dt,dy,dx] * xt[b,i,t+dt,y+dy-kh/2,x+dx-kw/2]
  * where xt is (2*(kt/2) - n_cache) zero frames, then the cache frames, then x, with zero
- * padding kh/2, kw/2 in space.
+ * padding kh/2, kw/2 in space. The sums accumulate in float32 ("Precision").
  *
- *  x       [B, Cin, t, h, w] (NCTHW) or [B, t, h, w, Cin] (NTHWC), element type dtype.
- *  cache   n_cache frames in the same layout ([B, Cin, n_cache, h, w] / [B, n_cache, h, w,
- *          Cin]), dtype; may be NULL when n_cache == 0. Requires 0 <= n_cache <= 2 and
- *          n_cache == 0 when kt == 1. In NTHWC both are read in place.
- *  weight  [Cout, Cin, kt, kh, kw] with kt in {1, 3}, kh, kw in {1, 3}; bias [Cout].
- *  y       [B, Cout, t, h, w] / [B, t, h, w, Cout], dtype.
- *  Requires Cin a multiple of 8, t <= 6.
+ *  x        [B, Cin, t, h, w] (NCTHW) or [B, t, h, w, Cin] (NTHWC), element type dtype.
+ *  cache    n_cache frames in the same layout ([B, Cin, n_cache, h, w] / [B, n_cache, h, w,
+ *           Cin]), dtype; may be NULL when n_cache == 0. Requires 0 <= n_cache <= 2 and
+ *           n_cache == 0 when kt == 1. In NTHWC both are read in place.
+ *  weight   [Cout, Cin, kt, kh, kw] with kt in {1, 3}, kh, kw in {1, 3}; bias [Cout].
+ *  y        [B, Cout, t, h, w] / [B, t, h, w, Cout] of element type y_dtype. y_dtype == dtype
+ *           stores each sum + bias rounded to dtype; y_dtype = WANVAE_F32 with dtype =
+ *           WANVAE_BF16 stores the float32 sum + bias unrounded. A float32 conv with a bf16
+ *           y_dtype -> WANVAE_EDTYPE.
+ *  cache_out  NULL, or the updated cache ("Causal caches": the last frames of cache ++ x):
+ *           n_out = min(2, n_cache + t) frames, [B, Cin, n_out, h, w] / [B, n_out, h, w, Cin],
+ *           dtype, written after y. It may be the cache buffer itself when n_cache == 2 (the
+ *           in-place update); otherwise it must not overlap x, cache or y.
+ *  Requires Cin a multiple of 8, Cout a multiple of 4, t <= 6, and x, cache, y, cache_out
+ *  16-byte aligned (else WANVAE_EARG); y must not alias x or cache.
+ *  Workspace: wanvae_causal_conv3d_workspace_size (its size bounds every kernel 1 <= kt*kh*kw
+ *  <= 27 for Cout output channels).
  */
 int wanvae_causal_conv3d_workspace_size(int64_t B, int64_t Cin, int64_t Cout, int64_t t, int64_t h,
                                         int64_t w, int64_t n_cache, int32_t layout, int32_t dtype,
-                                        size_t *bytes);
+                                        int32_t y_dtype, size_t *bytes);
 int wanvae_causal_conv3d(const void *x, const void *cache, int64_t B, int64_t Cin, int64_t t,
                          int64_t h, int64_t w, int64_t n_cache, const wanvae_tensor *weight,
                          const wanvae_tensor *bias, int32_t layout, int32_t dtype, void *y,
-                         void *workspace, size_t workspace_bytes, void *stream);
+                         int32_t y_dtype, void *cache_out, void *workspace, size_t workspace_bytes,
+                         void *stream);
 
 /*
  * wanvae_attn_block -- the mid-block attention block (WanAttentionBlock, "The parts":
@@ -123,7 +137,8 @@ int wanvae_causal_conv3d(const void *x, const void *cache, int64_t B, int64_t Ci
  *  gamma   C elements; qkv_w [3C, C, 1, 1] (or [3C, C]); qkv_b [3C];
  *          proj_w [C, C, 1, 1] (or [C, C]); proj_b [C].
  *  y       same shape and layout as x. Must not alias x.
- *  Requires C a multiple of 64 and <= 1024.
+ *  Requires C in {64, 128, 256, 384, 512, 1024} (the widths the attention kernels run),
+ *  else WANVAE_ESHAPE.
  */
 int wanvae_attn_block_workspace_size(int64_t B, int64_t C, int64_t T, int64_t h, int64_t w,
                                      int32_t layout, int32_t dtype, size_t *bytes);

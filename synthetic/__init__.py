@@ -105,6 +105,34 @@ def gen_weights(base: int, seed: int, bias_std: float | None = None) -> dict[str
     return out
 
 
+def exact_sum_weights(base: int, seed: int) -> dict[str, np.ndarray]:
+    """Weights under which every conv output is its bias plus at most one product, so a
+    float32 accumulation gives the exact sum in any order: each output channel of a conv has
+    a single nonzero tap (a random input channel and tap) of value +-1 or +-1/2 (+-1/4 or
+    +-1/2 for conv_out); the attention's output projection is zero. Biases are multiples of
+    2^-8 in (-1/4, 1/4), gammas 1 + k/128 with |k| <= 16: every value is exact in bfloat16."""
+    shapes = weight_shapes(base)
+    out = {}
+    for name, shape in shapes.items():
+        g = stream(seed, name)
+        if name.endswith(".gamma"):
+            out[name] = (1.0 + g.integers(-16, 17, size=shape) / 128.0).astype(np.float32)
+        elif name.endswith(".bias"):
+            out[name] = (g.integers(-63, 64, size=shape) / 256.0).astype(np.float32)
+        else:
+            w = np.zeros(shape, np.float32)
+            if not name.endswith("attentions.0.proj.weight"):
+                co, ci = shape[0], shape[1]
+                taps = int(np.prod(shape[2:]))
+                flat = w.reshape(co, ci, taps)
+                small = name == "decoder.conv_out.weight"
+                mag = np.where(g.integers(0, 2, size=co) == 0, 0.5, 0.25 if small else 1.0)
+                sign = np.where(g.integers(0, 2, size=co) == 0, 1.0, -1.0)
+                flat[np.arange(co), g.integers(0, ci, size=co), g.integers(0, taps, size=co)] = mag * sign
+            out[name] = w
+    return out
+
+
 @dataclass(frozen=True)
 class DecodeConfig:
     name: str

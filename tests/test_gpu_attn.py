@@ -2,9 +2,12 @@
 
 The block returns x + branch with branch = proj(softmax(q k^T / sqrt(C)) v). x dominates
 the output, so the branch (out - x) is also compared relative to its own size: fp32 to 1e-5,
-bf16 to 1.5e-2 (every output also within 3e-2 or two bf16 spacings at its magnitude). The oracle
-keeps the softmax probabilities exact; the bf16 kernel rounds them to bf16 for the MFMA.
-A "peaked" variant scales q by 8 so the softmax concentrates on few keys.
+bf16 to 1.5e-2 in L2; and element by element, where in bf16 each output may differ by one
+spacing of the output (the final rounding of x + branch) plus one spacing of the branch (the
+rounding of proj) plus 1/16 of the branch's RMS (the bf16 probabilities and the rounding of O
+ahead of the projection). The oracle keeps the softmax probabilities exact; the bf16 kernel
+rounds them to bf16 for the MFMA. A "peaked" variant scales q by 8 so the softmax concentrates
+on few keys.
 """
 import numpy as np
 import pytest
@@ -39,22 +42,36 @@ def run(x, ws, mode, layout):
     return y.transpose(0, 4, 1, 2, 3) if layout == "nthwc" else y
 
 
-def compare(got, x, ws, mode, what):
-    xr = rounded(x, mode)
-    want = oracle.attention(xr, *[rounded(a, mode) for a in ws], oracle.Prec(mode))
+def branch_bound(want, br):
+    """Element-wise bf16 bound on |got - want| (module docstring)."""
+    rms = float(np.sqrt(np.mean(br * br)))
+    return bf16_ulp(np.abs(want)) + bf16_ulp(np.abs(br)) + rms / 16
+
+
+def check_outputs(got, want, xr, mode, what):
     d = np.abs(got.astype(np.float64) - want)
     br = want.astype(np.float64) - xr
     rel = np.linalg.norm(got - want) / np.linalg.norm(br)
-    say(what, "max", d.max(), "branch rel", rel)
     if mode == "fp32":
+        say(what, "max", d.max(), "branch rel", rel)
         assert d.max() <= 1e-4 * max(1.0, np.abs(br).max()), d.max()
         assert rel <= 1e-5
-    else:
-        # the output x + branch is rounded to bf16 at its own magnitude (outside [-1, 1] one
-        # spacing can exceed 3e-2); the branch itself must agree to 1.5%
-        lim = np.maximum(3e-2, 2 * bf16_ulp(np.abs(want)))
-        assert np.all(d <= lim), d.max()
-        assert rel <= 1.5e-2, rel
+        return
+    lim = branch_bound(want, br)
+    say(what, "max", d.max(), "branch rel", rel, "branch rms", float(np.sqrt(np.mean(br * br))),
+        "max diff / bound", float((d / lim).max()))
+    # the output x + branch is rounded to bf16 at its own magnitude (outside [-1, 1] one
+    # spacing can exceed 3e-2); the branch itself must agree to 1.5% in L2, and each output
+    # within the element-wise bound
+    assert np.all(d <= np.maximum(3e-2, 2 * bf16_ulp(np.abs(want)))), d.max()
+    assert rel <= 1.5e-2, rel
+    assert np.all(d <= lim), float((d / lim).max())
+
+
+def compare(got, x, ws, mode, what):
+    xr = rounded(x, mode)
+    want = oracle.attention(xr, *[rounded(a, mode) for a in ws], oracle.Prec(mode))
+    check_outputs(got, want, xr, mode, what)
 
 
 @pytest.mark.parametrize("mode", ["fp32", "bf16"])
@@ -91,7 +108,7 @@ def test_attn_full_size_sampled_frames(mode):
     xt = to_dev(x, mode).permute(0, 2, 3, 4, 1).contiguous()
     y = wanvae.wanvae_attn_block(xt, *[to_dev(a, mode) for a in ws], layout="nthwc")
     torch.cuda.synchronize()
-    for f in (0, 17, 30):
+    for f in range(cfg.T):
         got = to_np(y[:, f:f + 1]).transpose(0, 4, 1, 2, 3)
         compare(got, x[:, :, f:f + 1], ws, mode, f"frame {f} {mode}")
 
@@ -118,14 +135,4 @@ def test_attn_720p_frames_sampled_rows(name, mode):
         got = to_np(y[0, f].reshape(S, C)[torch.from_numpy(rows).to(y.device)])
         want = oracle.attention_rows(xr[0, :, f], *wr, P, rows)
         xrows = xr[0, :, f].reshape(C, S).T[rows]
-        d = np.abs(got.astype(np.float64) - want)
-        br = want - xrows
-        rel = np.linalg.norm(got - want) / np.linalg.norm(br)
-        say(name, mode, "frame", f, "max", d.max(), "branch rel", rel)
-        if mode == "fp32":
-            assert d.max() <= 1e-4 * max(1.0, np.abs(br).max()), d.max()
-            assert rel <= 1e-5
-        else:
-            lim = np.maximum(3e-2, 2 * bf16_ulp(np.abs(want)))
-            assert np.all(d <= lim), d.max()
-            assert rel <= 1.5e-2, rel
+        check_outputs(got, want, xrows, mode, f"{name} {mode} frame {f}")

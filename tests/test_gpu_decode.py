@@ -167,7 +167,9 @@ def test_decode_pipeline_matches_chunk_order_bit_for_bit(pipeline, mode):
 
 def test_small32_decode_pipeline_matches_chunk_order_bit_for_bit(pipeline):
     """decoder_base_dim 32, T = 5, 8x12 latent: the halo-tile kernels and the level-0 split K
-    on both streams; on and off agree bit for bit."""
+    on both streams; on and off agree bit for bit, and the video matches the oracle over all
+    five chunks (three in the steady state, where the halo tiles read two frames of time
+    history), by the multi-chunk bf16 gate."""
     cfg = synthetic.DECODE_CONFIGS["small32"]
     z = synthetic.normal(9, "latents_pipe32", (1, 48, 5, cfg.h, cfg.w))
     W = cfg.weights()
@@ -178,6 +180,9 @@ def test_small32_decode_pipeline_matches_chunk_order_bit_for_bit(pipeline):
     off = gpu_decode(z, W, "bf16")
     assert torch.equal(on, off)
     assert torch.isfinite(on).all()
+    say("small32 T5 oracle (bf16 and fp32 modes)")
+    want = oracle.decode(z, W, "bf16")
+    gate_bf16_scale(to_np(on), want, oracle.decode(z, W, "fp32").astype(np.float64), "small32 T5 bf16")
 
 
 def test_concurrent_decodes_on_two_threads_and_streams():
@@ -310,3 +315,23 @@ def test_full_decode_first_frames_match_oracle_samples(config, mode):
         del ordered
     del video
     torch.cuda.empty_cache()
+
+
+def test_binding_rejects_host_weights_and_wrong_outputs(tiny):
+    """The binding refuses a weight left on the host, a video of the wrong element type and a
+    conv cache on another device than x, before the library sees any pointer."""
+    z, W = tiny
+    zt = torch.from_numpy(z).to(dev())
+    Wt = {k: torch.from_numpy(v).to(dev()) for k, v in W.items()}
+    host = dict(Wt)
+    host["decoder.conv_out.weight"] = torch.from_numpy(W["decoder.conv_out.weight"])
+    with pytest.raises(ValueError, match="decoder.conv_out.weight"):
+        wanvae.wanvae_decode(zt, host, torch.float32)
+    with pytest.raises(ValueError, match="element type"):
+        wanvae.wanvae_decode(zt, Wt, torch.float32, video=torch.empty(1, 3, 5, 64, 64, dtype=torch.bfloat16,
+                                                                       device=dev()))
+    x = torch.zeros(1, 16, 2, 4, 4, dtype=torch.bfloat16, device=dev())
+    w = torch.zeros(32, 16, 3, 3, 3, device=dev())
+    with pytest.raises(ValueError, match="cache"):
+        wanvae.wanvae_causal_conv3d(x, torch.zeros(1, 16, 2, 4, 4, dtype=torch.bfloat16), w,
+                                    torch.zeros(32, device=dev()))

@@ -1,0 +1,63 @@
+"""The bf16 decode's rounding points, bit for bit (GPU).
+
+With synthetic.exact_sum_weights every conv output is its bias plus at most one product, so
+the GPU's float32 sums equal the oracle's float64 ones exactly, in any order. The only
+differences left are those of the page's "Precision" section: where the decode rounds to
+bf16. The RMS norm (whose float32 sum of squares still differs from the oracle's float64 one in
+its last bits), the residual and DupUp3D sums, the time conv's interleave, the attention
+block's residual, unpatchify and clamp are then checked bit for bit: at least 99.9% of the
+video's values equal the oracle's, and every other one within one bf16 spacing (a norm whose
+float32 rounding lands on the other side of a bf16 rounding boundary moves one value by one
+spacing). fp32 decodes under the same weights agree with the oracle to float32 rounding.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+from _gpu import bf16_ulp, dev, say, to_np
+from video_vae_decoding_amd import wanvae
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # (base, B, T, h, w): the tiny decoder with two steady-state chunks (two frames of time-conv
+    # history) and a ragged latent; base 32 on 8 x 12 latents (128-channel levels: the halo-tile
+    # convs at levels 1-3, the level-0 split K); base 96 (the 4-wave 384-wide attention, and the
+    # generic norm at 96 and 192 channels)
+    (16, 2, 4, 3, 5),
+    (32, 1, 3, 8, 12),
+    (96, 1, 2, 2, 3),
+]
+
+
+def decode_both(base, B, T, h, w, mode):
+    W = synthetic.exact_sum_weights(base, 21)
+    z = synthetic.normal(21, "latents", (B, synthetic.Z_DIM, T, h, w))
+    Wt = {k: torch.from_numpy(v).to(dev()) for k, v in W.items()}
+    got = wanvae.wanvae_decode(torch.from_numpy(z).to(dev()), Wt, torch.bfloat16 if mode == "bf16" else torch.float32)
+    torch.cuda.synchronize()
+    return to_np(got).astype(np.float64), oracle.decode(z, W, mode).astype(np.float64)
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_exact_sum_decode_bf16_bit_level(case):
+    say("exact-sum bf16 decode", case)
+    got, want = decode_both(*case, "bf16")
+    assert got.shape == want.shape
+    d = np.abs(got - want)
+    exact = float(np.mean(d == 0))
+    ulp = bf16_ulp(np.maximum(np.abs(got), np.abs(want)))
+    say(case, "bit-equal", exact, "max diff", d.max(), "max diff / spacing", (d / ulp).max())
+    assert exact >= 0.999, exact
+    assert np.all(d <= ulp), (d / ulp).max()
+
+
+@pytest.mark.parametrize("case", CASES[:2])
+def test_exact_sum_decode_fp32(case):
+    say("exact-sum fp32 decode", case)
+    got, want = decode_both(*case, "fp32")
+    d = np.abs(got - want)
+    say(case, "max diff", d.max(), "bit-equal", float(np.mean(d == 0)))
+    assert d.max() <= 1e-5, d.max()

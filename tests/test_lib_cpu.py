@@ -25,7 +25,7 @@ def test_library_exports_every_declared_function():
     L = W.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.wanvae_version() >= 100
+    assert L.wanvae_version() >= 200
 
 
 def host_weights(base=16):
@@ -106,6 +106,14 @@ def test_gamma_of_any_shape_with_C_elements_is_accepted():
 
 def test_other_topology_is_etopology():
     assert call_decode(host_weights(base=8)) == W.ETOPOLOGY
+    # widths the mid-block attention does not run (4 * base = 192, 320, 448): rejected with the
+    # other arguments, before any launch
+    for base in (48, 80, 112):
+        assert call_decode(host_weights(base=base)) == W.ETOPOLOGY, base
+        assert "decoder_base_dim" in W.lib().wanvae_last_error().decode()
+        assert ws_size(host_weights(base=base))[0] == W.ETOPOLOGY
+    for base in (16, 32, 64, 96, 128):
+        assert ws_size(host_weights(base=base))[0] == W.OK, base
     wts = host_weights()
     wts["post_quant_conv.weight"] = torch.zeros(16, 16, 1, 1, 1)
     assert call_decode(wts) == W.ETOPOLOGY
@@ -142,13 +150,24 @@ def test_conv_and_attention_validation():
         a = {**args, **kw}
         return L.wanvae_causal_conv3d(a["x"], a["cache"], a["B"], a["Cin"], a["t"], a["h"], a["w"], a["n"],
                                       ctypes.byref(w), ctypes.byref(b), kw.get("layout", 0), kw.get("dtype", 0),
-                                      4096, 4096, 1 << 40, None)
+                                      kw.get("y", 8192), kw.get("y_dtype", kw.get("dtype", 0)), kw.get("cache_out"),
+                                      4096, 1 << 40, None)
     assert conv(dtype=3) == W.EDTYPE
+    assert conv(dtype=W.BF16, y_dtype=5) == W.EDTYPE
+    assert conv(dtype=W.F32, y_dtype=W.BF16) == W.EDTYPE   # a float32 conv returns float32
+    assert "y_dtype" in L.wanvae_last_error().decode()
     assert conv(Cin=20) == W.ESHAPE        # not a multiple of 8 / does not match the weight
     assert conv(n=3) == W.ESHAPE
     assert conv(t=7) == W.ESHAPE
     assert conv(cache=None) == W.EARG
     assert conv(layout=5) == W.EARG
+    assert conv(x=4096 + 8) == W.EARG      # 16-byte alignment
+    assert conv(y=8192 + 4, y_dtype=W.F32) == W.EARG
+    assert conv(cache_out=12288 + 2) == W.EARG
+    assert conv(y=4096) == W.EARG          # y aliases x
+    assert conv(cache_out=8192) == W.EARG  # cache_out aliases y
+    assert conv(cache_out=4096) == W.EARG  # cache_out aliases x
+    assert conv(n=1, cache_out=4096 + 16, cache=4096 + 16) == W.EARG  # in place needs two cache frames
     g = W.tensor_struct("gamma", torch.zeros(64))
     qw = W.tensor_struct("qkv_w", torch.zeros(192, 64, 1, 1))
     qb = W.tensor_struct("qkv_b", torch.zeros(192))
@@ -160,6 +179,8 @@ def test_conv_and_attention_validation():
                                    ctypes.byref(pw), ctypes.byref(pb), dtype, y, 4096, 1 << 40, None)
     assert attn(dtype=9) == W.EDTYPE
     assert attn(C=96) == W.ESHAPE
+    assert attn(C=192) == W.ESHAPE         # a multiple of 64 the attention kernels do not run
+    assert "384" in L.wanvae_last_error().decode()
     assert attn(y=4096) == W.EARG
     assert attn(gam=W.tensor_struct("gamma", torch.zeros(63))) == W.ESHAPE
 

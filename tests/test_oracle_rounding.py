@@ -154,3 +154,23 @@ def test_residual_block_matches_torch_bf16_arithmetic():
     # the unrounded sum would not be a bf16 value in most positions
     unrounded = residual_block(x, W, name, {}, oracle.Prec("fp32"))
     assert np.mean(unrounded == want) < 0.5
+
+
+@pytest.mark.parametrize("base,h,w,T", [(16, 3, 5, 4), (32, 4, 6, 2)])
+def test_exact_sum_weights_make_the_decode_independent_of_the_summation_order(base, h, w, T):
+    """Under synthetic.exact_sum_weights every conv output is its bias plus at most one product
+    (each a bf16 times a power of two), so its float32 sum is exact in any order: the oracle's
+    bf16 decode with float64 sums and with float32 sums agree bit for bit. What remains are the
+    rounding points themselves, which move the video well away from the fp32 decode. This is
+    the construction the GPU's bit-level bf16 decode test relies on."""
+    W = synthetic.exact_sum_weights(base, 3)
+    z = synthetic.normal(3, "latents", (1, synthetic.Z_DIM, T, h, w))
+    a = oracle.decode(z, W, "bf16")
+    assert np.array_equal(a, oracle.decode(z, W, "bf16", acc="f32"))
+    f = oracle.decode(z, W, "fp32")
+    assert np.mean(np.abs(a.astype(np.float64) - f)) > 1e-4
+    for k, v in W.items():
+        assert _is_bf16(v), k
+        if k.endswith(".weight"):
+            nz = (v.reshape(v.shape[0], -1) != 0).sum(axis=1)
+            assert np.all(nz == (0 if k.endswith("attentions.0.proj.weight") else 1)), k

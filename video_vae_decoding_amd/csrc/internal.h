@@ -21,6 +21,8 @@ enum Epilogue {
   kEpiInterleave = 1,  // time conv: channel c < outC -> frame 2t, channel outC + c -> frame 2t+1
   kEpiVideo = 2,       // unpatchify + clamp into the NCTHW video
   kEpiQKV = 3,         // 1x1 conv C -> 3C: q, k as [frame][S][C], v transposed as [frame][C][Sp]
+  kEpiFramesF32 = 4,   // as kEpiFrames, but the float32 sums + bias are stored unrounded as float32
+                       // (a bf16 conv with a float32 output; no residual or DupUp3D term)
 };
 
 struct ConvArgs {
@@ -111,13 +113,18 @@ struct TileBlendArgs {
   int VH, VW, oy, ox, keep_h, keep_w;
 };
 hipError_t launch_tile_blend(const TileBlendArgs& a, int dtype, hipStream_t s);
+// rows x row_bytes bytes: dst + r * dst_pitch <- src + r * src_pitch (pitches in bytes); the
+// regions must not overlap
+hipError_t launch_copy_rows(const void* src, int64_t src_pitch, void* dst, int64_t dst_pitch, int64_t row_bytes,
+                            int64_t rows, hipStream_t s);
 // src [planes][h][w] (elements of esize bytes) rows y0.. x columns x0.. -> dst [planes][th][tw]
 hipError_t launch_crop(const void* src, void* dst, int esize, int64_t planes, int h, int w, int y0, int x0, int th,
                        int tw, hipStream_t s);
 
 hipError_t launch_conv(const ConvArgs& a, int dtype, int tile, hipStream_t s);
-// whether a halo-tile kernel handles this conv (bf16, 3x3 spatial, Cin % 32; tile 10: Cout % 128 and
-// the frame epilogue; tile 11: Cout <= 16 and the video epilogue; tile 12 as tile 10)
+// whether a halo-tile kernel handles this conv (bf16, 3x3 spatial, Cin % 32, an input frame of
+// fewer than 2^31 bytes; tiles 10, 12, 13: Cout % 128 and a frame epilogue; tile 11: Cout <= 16
+// and the video epilogue)
 bool conv_halo_supported(const ConvArgs& a, int dtype, int tile);
 hipError_t launch_norm(const NormArgs& a, int dtype, hipStream_t s);
 bool attn_supported(int C, int dtype);

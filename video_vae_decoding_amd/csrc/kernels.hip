@@ -124,6 +124,12 @@ __device__ __forceinline__ int vt_slot(int pix) {
 template <typename T>
 __device__ __forceinline__ void conv_epilogue(const ConvArgs& a, int t, int b, int y, int x, int c, float v[4]) {
   using X = Elem<T>;
+  if (a.mode == kEpiFramesF32) {
+    // the float32 sums + bias, unrounded, as float32 frames (c and outC are multiples of 4)
+    float* o = (float*)a.out[t] + b * a.out_bs[t] + ((int64_t)y * a.Wo + x) * a.outC + c;
+    *(float4*)o = make_float4(v[0], v[1], v[2], v[3]);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) v[i] = X::R(v[i]);
   const int64_t pix = (int64_t)y * a.Wo + x;
@@ -767,8 +773,9 @@ __global__ void __launch_bounds__(64 * WGC * WGP, MINB) k_conv_dma(const ConvArg
     }
     return;
   }
-  if constexpr (ES == 4) {
-    // fp32: each lane finishes its own 4 channels of each position (conv_epilogue: every mode)
+  if (ES == 4 || a.mode == kEpiFramesF32) {
+    // fp32, or a bf16 conv with a float32 output: each lane finishes its own 4 channels of
+    // each position (conv_epilogue: every mode)
 #pragma unroll
     for (int ip = 0; ip < TPN; ++ip) {
       const int m = m0 + wp * WP + ip * 16 + (lane & 15);
@@ -894,13 +901,19 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(const ConvArgs a) {
     s8[4] += x1.x, s8[5] += x1.y, s8[6] += x1.z, s8[7] += x1.w;
   }
   const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-#pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = bf2f(f2bf(s8[e] + bb[e]));
   const int x = (int)(m % a.Wo);
   int64_t q = m / a.Wo;
   const int y = (int)(q % a.Ho);
   q /= a.Ho;
   const int b = (int)(q % a.B), t = (int)(q / a.B);
+  if (a.mode == kEpiFramesF32) {
+    float* o = (float*)a.out[t] + b * a.out_bs[t] + ((int64_t)y * a.Wo + x) * a.outC + c;
+    *(float4*)o = make_float4(s8[0] + bb[0], s8[1] + bb[1], s8[2] + bb[2], s8[3] + bb[3]);
+    *(float4*)(o + 4) = make_float4(s8[4] + bb[4], s8[5] + bb[5], s8[6] + bb[6], s8[7] + bb[7]);
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = bf2f(f2bf(s8[e] + bb[e]));
   epilogue8_bf16(a, t, b, y, x, c, v);
 }
 
@@ -1206,6 +1219,24 @@ __global__ void __launch_bounds__(64 * WGC * WGP, 1) k_conv_halo(const ConvArgs 
         if (y < a.Ho && x < a.Wo && c < a.Cout)
           *(float4*)(a.part + ((int64_t)kz * M + m) * a.Cout + c) =
               make_float4(acc[ic][ip][0], acc[ic][ip][1], acc[ic][ip][2], acc[ic][ip][3]);
+      }
+    }
+    return;
+  }
+  if (a.mode == kEpiFramesF32) {
+    // a float32 output: each lane stores its own 4 channels of each position, sums + bias
+#pragma unroll
+    for (int ip = 0; ip < TPN; ++ip) {
+      const int p = wp * WP + ip * 16 + (lane & 15);
+      const int y = Y0 + p / TPX, x = X0 + p % TPX;
+#pragma unroll
+      for (int ic = 0; ic < TCN; ++ic) {
+        const int c = c0 + wc * WC + ic * 16 + 4 * (lane >> 4);
+        if (y < a.Ho && x < a.Wo && c < a.Cout) {
+          const float4 bb = *(const float4*)(a.bias + c);
+          float v[4] = {acc[ic][ip][0] + bb.x, acc[ic][ip][1] + bb.y, acc[ic][ip][2] + bb.z, acc[ic][ip][3] + bb.w};
+          conv_epilogue<T>(a, t, b, y, x, c, v);
+        }
       }
     }
     return;
@@ -1920,12 +1951,16 @@ static hipError_t conv_halo_go(const ConvArgs& a, hipStream_t s) {
 }
 
 bool conv_halo_supported(const ConvArgs& a, int dtype, int tile) {
-  const bool geometry = dtype == kBF16 && a.kh == 3 && a.kw == 3 && (a.kt == 1 || a.kt == 3) && a.Cin % 32 == 0 &&
+  // the kernel addresses an input frame with 32-bit byte offsets and marks padding with the
+  // offset 2^31: a frame (one batch element) must hold fewer bytes than that
+  const bool small = (int64_t)a.Hin * a.Win * a.Cin * 2 < ((int64_t)1 << 31);
+  const bool geometry = dtype == kBF16 && small && a.kh == 3 && a.kw == 3 && (a.kt == 1 || a.kt == 3) &&
+                        a.Cin % 32 == 0 &&
                         (!a.up || (a.Ho % 2 == 0 && a.Wo % 2 == 0 && a.Hin * 2 == a.Ho && a.Win * 2 == a.Wo)) &&
                         (a.up || (a.Hin == a.Ho && a.Win == a.Wo));
   if (tile == kTileHalo16x16x32)  // conv_out: up to 16 channels, the unpatchify + clamp store
     return geometry && a.Cout <= 16 && a.Cout % 4 == 0 && a.mode == kEpiVideo;
-  return geometry && a.Cout % 128 == 0 && a.mode == kEpiFrames;
+  return geometry && a.Cout % 128 == 0 && (a.mode == kEpiFrames || a.mode == kEpiFramesF32);
 }
 
 hipError_t launch_conv(const ConvArgs& a, int dtype, int tile, hipStream_t s) {

@@ -2,6 +2,8 @@
 // they overlap (the diffusers PR page "Implement tiled VAE encoding/decoding for Wan model";
 // the blend rule is not on the page and is read as a linear ramp with the composed tile above,
 // then the composed tile to the left). Both are HBM-bound copies with a few flops per element.
+// Also the strided row copy that writes a single causal conv's updated cache (the last two
+// frames of cache ++ chunk, FastVideo's "wan22_vae_decode reference.py" page, "Causal caches").
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -78,6 +80,17 @@ __global__ void __launch_bounds__(256) k_crop(const T* __restrict__ src, T* __re
   }
 }
 
+// rows of units_per_row U-sized units: dst row r at dst + r * dp, src row r at src + r * sp
+template <typename U>
+__global__ void __launch_bounds__(256) k_copy_rows(const char* __restrict__ src, int64_t sp, char* __restrict__ dst,
+                                                   int64_t dp, int64_t units_per_row, int64_t rows) {
+  const int64_t n = units_per_row * rows;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / units_per_row, u = i - r * units_per_row;
+    ((U*)(dst + r * dp))[u] = ((const U*)(src + r * sp))[u];
+  }
+}
+
 int grid_for(int64_t n) { return (int)std::min<int64_t>((n + 255) / 256, 4096); }
 
 }  // namespace
@@ -89,6 +102,30 @@ hipError_t launch_tile_blend(const TileBlendArgs& a, int dtype, hipStream_t s) {
     hipLaunchKernelGGL(k_tile_blend<uint16_t>, dim3(grid_for(n)), dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(k_tile_blend<float>, dim3(grid_for(n)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_rows(const void* src, int64_t src_pitch, void* dst, int64_t dst_pitch, int64_t row_bytes,
+                            int64_t rows, hipStream_t s) {
+  if (row_bytes <= 0 || rows <= 0) return hipSuccess;
+  const uint64_t all = (uint64_t)(uintptr_t)src | (uint64_t)(uintptr_t)dst | (uint64_t)src_pitch |
+                       (uint64_t)dst_pitch | (uint64_t)row_bytes;
+  const char* sp = (const char*)src;
+  char* dp = (char*)dst;
+  if (all % 16 == 0) {
+    const int64_t u = row_bytes / 16;
+    hipLaunchKernelGGL(k_copy_rows<uint4>, dim3(grid_for(u * rows)), dim3(256), 0, s, sp, src_pitch, dp, dst_pitch, u,
+                       rows);
+  } else if (all % 4 == 0) {
+    const int64_t u = row_bytes / 4;
+    hipLaunchKernelGGL(k_copy_rows<uint32_t>, dim3(grid_for(u * rows)), dim3(256), 0, s, sp, src_pitch, dp,
+                       dst_pitch, u, rows);
+  } else {
+    if (all % 2 != 0) return hipErrorInvalidValue;
+    const int64_t u = row_bytes / 2;
+    hipLaunchKernelGGL(k_copy_rows<uint16_t>, dim3(grid_for(u * rows)), dim3(256), 0, s, sp, src_pitch, dp,
+                       dst_pitch, u, rows);
+  }
   return hipGetLastError();
 }
 

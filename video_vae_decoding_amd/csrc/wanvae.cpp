@@ -274,8 +274,10 @@ static int build_topology(const WeightMap& m, Topology& tp) {
   if (pq == m.end()) return fail(WANVAE_EMISSING, "missing parameter post_quant_conv.weight");
   if (pq->second->ndim != 5 || pq->second->shape[0] != 48)
     return fail(WANVAE_ETOPOLOGY, "post_quant_conv.weight %s: the decoder needs z_dim 48", shape_str(pq->second).c_str());
-  if (base < 16 || base % 16 != 0 || 4 * base > 1024)
-    return fail(WANVAE_ETOPOLOGY, "decoder_base_dim %lld unsupported (needs a multiple of 16, at most 256)", (long long)base);
+  // the widths run on every kernel the decoder launches: the mid-block attention needs
+  // 4 * base in {64, 128, 256, 384, 512, 1024}
+  if (base < 16 || base % 16 != 0 || 4 * base > 1024 || !attn_supported(4 * (int)base, kBF16))
+    return fail(WANVAE_ETOPOLOGY, "decoder_base_dim %lld unsupported (16, 32, 64, 96, 128 or 256)", (long long)base);
   make_topology((int)base, tp);
   for (const ConvSpec& c : tp.convs) {
     const std::string wn = c.name + ".weight", bn = c.name + ".bias";
@@ -993,7 +995,7 @@ int wanvae_set_decode_pipeline(int on) {
   return WANVAE_OK;
 }
 
-int wanvae_version(void) { return 100; }
+int wanvae_version(void) { return 200; }
 
 int wanvae_decode_workspace_size(int64_t B, int64_t T, int64_t h, int64_t w, const wanvae_tensor* weights,
                                  int64_t n_weights, int32_t dtype, size_t* bytes) {
@@ -1219,12 +1221,21 @@ int wanvae_decode_tiled(const void* z, int32_t z_dtype, int64_t B, int64_t T, in
 
 // ---------------------------------------------------------------- single causal conv
 
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
 static int conv_validate(const void* x, const void* cache, int64_t B, int64_t Cin, int64_t t, int64_t h, int64_t w,
                          int64_t n_cache, const wanvae_tensor* weight, const wanvae_tensor* bias, int32_t layout,
-                         int32_t dtype, const void* y) {
+                         int32_t dtype, const void* y, int32_t y_dtype, const void* cache_out) {
   if (int rc = check_dtype(dtype, "dtype")) return rc;
+  if (int rc = check_dtype(y_dtype, "y_dtype")) return rc;
+  if (dtype == kF32 && y_dtype != kF32)
+    return fail(WANVAE_EDTYPE, "a float32 conv returns float32 (y_dtype must be WANVAE_F32)");
   if (layout != WANVAE_NCTHW && layout != WANVAE_NTHWC) return fail(WANVAE_EARG, "layout %d unknown", layout);
   if (!x || !y) return fail(WANVAE_EARG, "x and y must not be NULL");
+  if (!aligned16(x) || !aligned16(y) || !aligned16(cache) || !aligned16(cache_out))
+    return fail(WANVAE_EARG, "x, cache, y and cache_out must be 16-byte aligned");
+  if (y == x || (cache && y == cache) || (cache_out && (cache_out == x || cache_out == y)))
+    return fail(WANVAE_EARG, "y must not alias x or cache, and cache_out must not alias x or y");
   if (int rc = check_tensor(weight, "weight")) return rc;
   if (int rc = check_tensor(bias, "bias")) return rc;
   if (B < 1 || Cin < 1 || t < 1 || h < 1 || w < 1) return fail(WANVAE_ESHAPE, "B, Cin, t, h, w must be >= 1");
@@ -1240,49 +1251,39 @@ static int conv_validate(const void* x, const void* cache, int64_t B, int64_t Ci
   if (n_cache < 0 || n_cache > 2 || (kt == 1 && n_cache != 0))
     return fail(WANVAE_ESHAPE, "n_cache %lld (needs 0..2, and 0 for kt = 1)", (long long)n_cache);
   if (n_cache > 0 && !cache) return fail(WANVAE_EARG, "cache NULL with n_cache %lld", (long long)n_cache);
+  if (cache_out && cache_out == cache && n_cache != 2)
+    return fail(WANVAE_EARG, "cache_out may be the cache itself only when both hold 2 frames (n_cache %lld)",
+                (long long)n_cache);
   if (t + kt - 1 > kMaxFrames) return fail(WANVAE_ESHAPE, "t %lld too large (at most %d)", (long long)t, kMaxFrames - 2);
   if (B * h * w * (Cin > Cout ? Cin : Cout) > ((int64_t)1 << 31)) return fail(WANVAE_ESHAPE, "frame too large");
   return WANVAE_OK;
 }
 
+// frames of the updated cache: the last min(2, n_cache + t) of cache ++ x ("Causal caches")
+static int64_t cache_out_frames(int64_t n_cache, int64_t t) { return std::min<int64_t>(2, n_cache + t); }
+
 static size_t conv_ws(int64_t B, int64_t Cin, int64_t Cout, int64_t taps, int64_t t, int64_t h, int64_t w,
-                      int64_t n_cache, int32_t layout, int32_t dtype) {
+                      int64_t n_cache, int32_t layout, int32_t dtype, int32_t y_dtype) {
   Arena ar;
   ar.take((size_t)Cout * taps * Cin * esize(dtype));
   ar.take((size_t)Cout * 4);
   if (layout == WANVAE_NCTHW) {
     ar.take((size_t)(t + n_cache) * B * h * w * Cin * esize(dtype));
-    ar.take((size_t)t * B * h * w * Cout * esize(dtype));
+    ar.take((size_t)t * B * h * w * Cout * esize(y_dtype));
   }
   take_split(ar, t * B * h * w, Cout);
   return ar.used;
 }
 
-int wanvae_causal_conv3d_workspace_size(int64_t B, int64_t Cin, int64_t Cout, int64_t t, int64_t h, int64_t w,
-                                        int64_t n_cache, int32_t layout, int32_t dtype, size_t* bytes) {
-  g_err.clear();
-  if (!bytes) return fail(WANVAE_EARG, "bytes: NULL");
-  if (int rc = check_dtype(dtype, "dtype")) return rc;
-  *bytes = conv_ws(B, Cin, Cout, 27, t, h, w, n_cache, layout, dtype);
-  return WANVAE_OK;
-}
-
-int wanvae_causal_conv3d(const void* x, const void* cache, int64_t B, int64_t Cin, int64_t t, int64_t h, int64_t w,
-                         int64_t n_cache, const wanvae_tensor* weight, const wanvae_tensor* bias, int32_t layout,
-                         int32_t dtype, void* y, void* workspace, size_t workspace_bytes, void* stream) {
-  g_err.clear();
-  if (int rc = conv_validate(x, cache, B, Cin, t, h, w, n_cache, weight, bias, layout, dtype, y)) return rc;
+// Enqueues the conv on a workspace of at least conv_ws bytes (arguments already validated).
+static int conv_run(const void* x, const void* cache, int64_t B, int64_t Cin, int64_t t, int64_t h, int64_t w,
+                    int64_t n_cache, const wanvae_tensor* weight, const wanvae_tensor* bias, int32_t layout,
+                    int32_t dtype, void* y, int32_t y_dtype, void* cache_out, void* ws, hipStream_t st) {
   const int Cout = (int)weight->shape[0], kt = (int)weight->shape[2], kh = (int)weight->shape[3],
             kw = (int)weight->shape[4];
-  const size_t need = conv_ws(B, Cin, Cout, kt * kh * kw, t, h, w, n_cache, layout, dtype);
-  if (workspace && workspace_bytes < need)
-    return fail(WANVAE_EWORKSPACE, "workspace of %zu bytes, the conv needs %zu", workspace_bytes, need);
-  hipStream_t st = (hipStream_t)stream;
-  void* ws = workspace;
-  if (!ws) HIP_TRY(hipMallocAsync(&ws, need, st));
   Arena ar;
   ar.base = (char*)ws;
-  const size_t es = esize(dtype);
+  const size_t es = esize(dtype), yes = esize(y_dtype);
   const int64_t hw = h * w;
   const int tpad = 2 * (kt / 2);
   ConvW cw;
@@ -1293,7 +1294,7 @@ int wanvae_causal_conv3d(const void* x, const void* cache, int64_t B, int64_t Ci
   if (rc == WANVAE_OK && layout == WANVAE_NCTHW) {
     // convert to frames [n_cache + t][B][h][w][Cin] in the workspace
     void* xin = ar.take((size_t)(t + n_cache) * B * hw * Cin * es);
-    yout = ar.take((size_t)t * B * hw * Cout * es);
+    yout = ar.take((size_t)t * B * hw * Cout * yes);
     const int64_t fe = B * hw * Cin;
     hipError_t e = hipSuccess;
     if (n_cache)
@@ -1303,24 +1304,72 @@ int wanvae_causal_conv3d(const void* x, const void* cache, int64_t B, int64_t Ci
                                  (int)h, (int)w, st);
     if (e != hipSuccess) rc = fail(WANVAE_EHIP, "layout conversion: %s", hipGetErrorString(e));
     for (int k = 0; k < n_cache + t; ++k) in.push((char*)xin + k * fe * es, hw * Cin);
-    out = frames_of(yout, (int)t, B * hw * Cout, hw * Cout, es);
+    out = frames_of(yout, (int)t, B * hw * Cout, hw * Cout, yes);
   } else if (rc == WANVAE_OK) {
     // [B, frames, h, w, C]: frame k of batch b at base + (b * frames + k) * hwC; read and written in place
     for (int k = 0; k < n_cache; ++k) in.push((char*)cache + k * hw * Cin * es, n_cache * hw * Cin);
     for (int k = 0; k < t; ++k) in.push((char*)x + k * hw * Cin * es, t * hw * Cin);
-    out = frames_of(y, (int)t, hw * Cout, t * hw * Cout, es);
+    out = frames_of(y, (int)t, hw * Cout, t * hw * Cout, yes);
   }
   if (rc == WANVAE_OK) {
     SplitScope scope(take_split(ar, t * B * h * w, Cout));
     ConvCall cc;
-    cc.a.mode = kEpiFrames;
+    cc.a.mode = y_dtype == dtype ? kEpiFrames : kEpiFramesF32;
     set_out(cc.a, out, Cout);
     rc = run_conv(cw, in, (int)B, (int)h, (int)w, (int)h, (int)w, (int)t, false, cc, dtype, st);
   }
   if (rc == WANVAE_OK && layout == WANVAE_NCTHW) {
-    hipError_t e = launch_frames_to_ncthw(yout, y, dtype, (int)B, Cout, (int)t, (int)h, (int)w, st);
+    hipError_t e = launch_frames_to_ncthw(yout, y, y_dtype, (int)B, Cout, (int)t, (int)h, (int)w, st);
     if (e != hipSuccess) rc = fail(WANVAE_EHIP, "y layout: %s", hipGetErrorString(e));
   }
+  if (rc == WANVAE_OK && cache_out) {
+    // the updated cache, frame by frame in order: its frame j is frame n_cache + t - n_out + j
+    // of cache ++ x. A row is one (batch, channel) plane (NCTHW) or one batch element (NTHWC).
+    // Frame j reads a later or the same frame of the concatenation, so cache_out may be the
+    // cache itself (updated in place): each frame's copy is its own launch, in order.
+    const int64_t n_out = cache_out_frames(n_cache, t);
+    const int64_t fb = (layout == WANVAE_NCTHW ? hw : hw * Cin) * (int64_t)es;  // bytes of a frame in a row
+    const int64_t rows = layout == WANVAE_NCTHW ? B * Cin : B;
+    for (int64_t j = 0; j < n_out && rc == WANVAE_OK; ++j) {
+      const int64_t f = n_cache + t - n_out + j;
+      const bool from_cache = f < n_cache;
+      const char* src = from_cache ? (const char*)cache + f * fb : (const char*)x + (f - n_cache) * fb;
+      const int64_t src_pitch = (from_cache ? n_cache : t) * fb;
+      hipEvent_t e0 = prof_start(st);
+      hipError_t e = launch_copy_rows(src, src_pitch, (char*)cache_out + j * fb, n_out * fb, fb, rows, st);
+      if (e != hipSuccess) rc = fail(WANVAE_EHIP, "cache_out: %s", hipGetErrorString(e));
+      prof_stop(e0, WANVAE_KOTHER, 0, 2.0 * fb * rows, st);
+    }
+  }
+  return rc;
+}
+
+int wanvae_causal_conv3d_workspace_size(int64_t B, int64_t Cin, int64_t Cout, int64_t t, int64_t h, int64_t w,
+                                        int64_t n_cache, int32_t layout, int32_t dtype, int32_t y_dtype,
+                                        size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(WANVAE_EARG, "bytes: NULL");
+  if (int rc = check_dtype(dtype, "dtype")) return rc;
+  if (int rc = check_dtype(y_dtype, "y_dtype")) return rc;
+  *bytes = conv_ws(B, Cin, Cout, 27, t, h, w, n_cache, layout, dtype, y_dtype);
+  return WANVAE_OK;
+}
+
+int wanvae_causal_conv3d(const void* x, const void* cache, int64_t B, int64_t Cin, int64_t t, int64_t h, int64_t w,
+                         int64_t n_cache, const wanvae_tensor* weight, const wanvae_tensor* bias, int32_t layout,
+                         int32_t dtype, void* y, int32_t y_dtype, void* cache_out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (int rc = conv_validate(x, cache, B, Cin, t, h, w, n_cache, weight, bias, layout, dtype, y, y_dtype, cache_out))
+    return rc;
+  const int64_t taps = weight->shape[2] * weight->shape[3] * weight->shape[4];
+  const size_t need = conv_ws(B, Cin, weight->shape[0], taps, t, h, w, n_cache, layout, dtype, y_dtype);
+  if (workspace && workspace_bytes < need)
+    return fail(WANVAE_EWORKSPACE, "workspace of %zu bytes, the conv needs %zu", workspace_bytes, need);
+  hipStream_t st = (hipStream_t)stream;
+  void* ws = workspace;
+  if (!ws) HIP_TRY(hipMallocAsync(&ws, need, st));
+  int rc = conv_run(x, cache, B, Cin, t, h, w, n_cache, weight, bias, layout, dtype, y, y_dtype, cache_out, ws, st);
   if (!workspace) {
     hipError_t e = hipFreeAsync(ws, st);
     if (rc == WANVAE_OK && e != hipSuccess) rc = fail(WANVAE_EHIP, "hipFreeAsync: %s", hipGetErrorString(e));
@@ -1343,7 +1392,7 @@ static int attn_validate(const void* x, int32_t layout, int64_t B, int64_t C, in
     if (int rc = check_tensor(ts[i], nm[i])) return rc;
   if (B < 1 || T < 1 || h < 1 || w < 1 || C < 1) return fail(WANVAE_ESHAPE, "B, C, T, h, w must be >= 1");
   if (C % 64 != 0 || C > 1024 || !attn_supported((int)C, dtype))
-    return fail(WANVAE_ESHAPE, "C %lld unsupported (64, 128, 256, 512 or 1024)", (long long)C);
+    return fail(WANVAE_ESHAPE, "C %lld unsupported (64, 128, 256, 384, 512 or 1024)", (long long)C);
   if (numel(gamma) != C) return fail(WANVAE_ESHAPE, "gamma has %lld elements, expected %lld", (long long)numel(gamma), (long long)C);
   if (!(shape_is(qkv_w, {3 * C, C, 1, 1}) || shape_is(qkv_w, {3 * C, C})))
     return fail(WANVAE_ESHAPE, "qkv_w %s, expected [%lld, %lld, 1, 1]", shape_str(qkv_w).c_str(), (long long)(3 * C), (long long)C);

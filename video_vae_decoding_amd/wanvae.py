@@ -7,6 +7,12 @@ when it is missing.
 
 Status codes map to exceptions as FastVideo's "wan22_vae_decode reference.py" page raises
 them: a bad dtype is a ValueError, a missing parameter a KeyError.
+
+Before any library call every tensor is checked: inputs (z, x, cache, weights) must live on one
+CUDA device, with the element types and ranks the call takes (x and cache are made contiguous,
+weights must be); outputs (video, y, cache_out) and a given workspace must be contiguous tensors
+of exactly the shape and element type the call writes, on that device. A tensor that fails is a
+ValueError, so the kernels never see a host pointer or a buffer smaller than they address.
 """
 from __future__ import annotations
 
@@ -52,8 +58,10 @@ def lib() -> ctypes.CDLL:
         T = ctypes.POINTER(wanvae_tensor)
         L.wanvae_decode_workspace_size.argtypes = [i64, i64, i64, i64, T, i64, i32, ctypes.POINTER(sz)]
         L.wanvae_decode.argtypes = [vp, i32, i64, i64, i64, i64, T, i64, i32, vp, vp, sz, vp]
-        L.wanvae_causal_conv3d_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64, i64, i32, i32, ctypes.POINTER(sz)]
-        L.wanvae_causal_conv3d.argtypes = [vp, vp, i64, i64, i64, i64, i64, i64, T, T, i32, i32, vp, vp, sz, vp]
+        L.wanvae_causal_conv3d_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64, i64, i32, i32, i32,
+                                                          ctypes.POINTER(sz)]
+        L.wanvae_causal_conv3d.argtypes = [vp, vp, i64, i64, i64, i64, i64, i64, T, T, i32, i32, vp, i32, vp, vp, sz,
+                                           vp]
         L.wanvae_attn_block_workspace_size.argtypes = [i64, i64, i64, i64, i64, i32, i32, ctypes.POINTER(sz)]
         L.wanvae_attn_block.argtypes = [vp, i32, i64, i64, i64, i64, i64, T, T, T, T, T, i32, vp, vp, sz, vp]
         L.wanvae_profile_enable.argtypes = [ctypes.c_int]
@@ -95,6 +103,37 @@ def dtype_code(dtype) -> int:
     return _DTYPES[dtype]
 
 
+def _on(t: torch.Tensor, name: str, device: torch.device) -> None:
+    """t must be a tensor on ``device`` (a CUDA device)."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor, not {type(t).__name__}")
+    if device.type != "cuda":
+        raise ValueError(f"{name} must be on a CUDA device, not {device}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the call runs on {device}")
+
+
+def _device_of(t: torch.Tensor, name: str) -> torch.device:
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor, not {type(t).__name__}")
+    d = t.device
+    if d.type == "cuda" and d.index is None:
+        d = torch.device("cuda", torch.cuda.current_device())
+    return d
+
+
+def _output(t: torch.Tensor, name: str, shape, dtype) -> None:
+    """A caller-given output: exactly ``shape`` and ``dtype``, contiguous."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor, not {type(t).__name__}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, the call writes {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has element type {t.dtype}, the call writes {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
 def tensor_struct(name: str | None, t: torch.Tensor) -> wanvae_tensor:
     if t.dim() > 5:
         raise ValueError(f"{name}: more than 5 dimensions")
@@ -104,8 +143,27 @@ def tensor_struct(name: str | None, t: torch.Tensor) -> wanvae_tensor:
     return wanvae_tensor(name.encode() if name is not None else None, t.data_ptr(), dtype_code(t.dtype), t.dim(), shape)
 
 
+def _weight_items(weights: Mapping[str, torch.Tensor]):
+    return [(k, v) for k, v in weights.items() if k.startswith(("decoder.", "post_quant_conv."))]
+
+
+def check_weights(weights: Mapping[str, torch.Tensor], device: torch.device | None = None) -> None:
+    """Every parameter the decoder reads: a contiguous float32 / bfloat16 tensor of at most
+    5 dimensions, on ``device`` when one is given."""
+    for k, v in _weight_items(weights):
+        if not isinstance(v, torch.Tensor):
+            raise ValueError(f"{k} must be a torch.Tensor, not {type(v).__name__}")
+        dtype_code(v.dtype)
+        if v.dim() > 5:
+            raise ValueError(f"{k}: more than 5 dimensions")
+        if not v.is_contiguous():
+            raise ValueError(f"{k}: not contiguous")
+        if device is not None:
+            _on(v, k, device)
+
+
 def tensor_table(weights: Mapping[str, torch.Tensor]):
-    items = [(k, v) for k, v in weights.items() if k.startswith(("decoder.", "post_quant_conv."))]
+    items = _weight_items(weights)
     arr = (wanvae_tensor * max(1, len(items)))()
     for i, (k, v) in enumerate(items):
         arr[i] = tensor_struct(k, v)
@@ -114,6 +172,14 @@ def tensor_table(weights: Mapping[str, torch.Tensor]):
 
 def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check_workspace(workspace: torch.Tensor | None, device) -> None:
+    if workspace is None:
+        return
+    if not isinstance(workspace, torch.Tensor) or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous torch.Tensor")
+    _on(workspace, "workspace", device)
 
 
 def _workspace(nbytes: int, device, workspace: torch.Tensor | None):
@@ -135,9 +201,7 @@ def wanvae_decode(z: torch.Tensor, weights: Mapping[str, torch.Tensor], dtype=to
                   video: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """decode(z [B, 48, T, h, w], weights) -> video [B, 3, 4T-3, 16h, 16w] of ``dtype`` on z's device."""
     dt = dtype_code(dtype)
-    if z.dim() != 5:
-        raise ValueError(f"z must be [B, 48, T, h, w], got {tuple(z.shape)}")
-    B, C, T, h, w = z.shape
+    B, T, h, w = _check_decode_args(z, weights, dtype, video, workspace)
     z = z.contiguous()
     arr, n = tensor_table(weights)
     need = decode_workspace_size(B, T, h, w, weights, dtype)
@@ -150,6 +214,25 @@ def wanvae_decode(z: torch.Tensor, weights: Mapping[str, torch.Tensor], dtype=to
 
 
 decode = wanvae_decode
+
+
+def _check_decode_args(z, weights, dtype, video, workspace):
+    """The decode's tensors, before any library call: z [B, 48, T, h, w] of float32 / bfloat16,
+    the weights, a given video [B, 3, 4T-3, 16h, 16w] of ``dtype``, all on z's CUDA device."""
+    device = _device_of(z, "z")
+    if z.dim() != 5 or z.shape[1] != 48:
+        raise ValueError(f"z must be [B, 48, T, h, w], got {tuple(z.shape)}")
+    dtype_code(z.dtype)
+    B, _, T, h, w = z.shape
+    if video is not None:
+        _output(video, "video", (B, 3, 4 * T - 3, 16 * h, 16 * w), dtype)
+    check_weights(weights)
+    _on(z, "z", device)
+    check_weights(weights, device)
+    if video is not None:
+        _on(video, "video", device)
+    _check_workspace(workspace, device)
+    return B, T, h, w
 
 
 def decode_tiled_workspace_size(B, T, h, w, weights: Mapping[str, torch.Tensor], dtype=torch.float32,
@@ -167,9 +250,7 @@ def wanvae_decode_tiled(z: torch.Tensor, weights: Mapping[str, torch.Tensor], dt
     """The spatially tiled decode: overlapping tiles of tile[0] x tile[1] video pixels every
     stride[0] x stride[1], each decoded on its own, blended where they overlap."""
     dt = dtype_code(dtype)
-    if z.dim() != 5:
-        raise ValueError(f"z must be [B, 48, T, h, w], got {tuple(z.shape)}")
-    B, C, T, h, w = z.shape
+    B, T, h, w = _check_decode_args(z, weights, dtype, video, workspace)
     z = z.contiguous()
     arr, n = tensor_table(weights)
     need = decode_tiled_workspace_size(B, T, h, w, weights, dtype, tile, stride)
@@ -184,36 +265,85 @@ def wanvae_decode_tiled(z: torch.Tensor, weights: Mapping[str, torch.Tensor], dt
 decode_tiled = wanvae_decode_tiled
 
 
-def conv_workspace_size(B, Cin, Cout, t, h, w, n_cache, layout, dtype) -> int:
+def conv_workspace_size(B, Cin, Cout, t, h, w, n_cache, layout, dtype, y_dtype=None) -> int:
     out = ctypes.c_size_t(0)
+    y_dtype = dtype if y_dtype is None else y_dtype
     check(lib().wanvae_causal_conv3d_workspace_size(B, Cin, Cout, t, h, w, n_cache, _LAYOUTS[layout], dtype_code(dtype),
-                                                    ctypes.byref(out)))
+                                                    dtype_code(y_dtype), ctypes.byref(out)))
     return out.value
 
 
 def wanvae_causal_conv3d(x: torch.Tensor, cache: torch.Tensor | None, weight: torch.Tensor, bias: torch.Tensor,
                          layout: str = "ncthw", y: torch.Tensor | None = None,
-                         workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """One causal conv of chunk x with ``cache`` frames of history; compute type = x.dtype."""
+                         workspace: torch.Tensor | None = None, y_dtype=None,
+                         cache_out: torch.Tensor | None = None, return_cache: bool = False):
+    """One causal conv of chunk x with ``cache`` frames of history; compute type = x.dtype.
+
+    ``y_dtype`` (default x.dtype) is the output's element type: torch.float32 with a bfloat16
+    x stores the float32 sums unrounded. ``cache_out`` (or, with ``return_cache``, a new tensor)
+    receives the updated cache, the last min(2, n_cache + t) frames of cache ++ x; it may be
+    ``cache`` itself when that holds 2 frames. Returns y, or (y, cache_out) with
+    ``return_cache``."""
+    if layout not in _LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(_LAYOUTS)}, not {layout!r}")
+    device = _device_of(x, "x")
     dtype = x.dtype
+    dtype_code(dtype)
+    y_dtype = dtype if y_dtype is None else y_dtype
+    dtype_code(y_dtype)
+    if x.dim() != 5:
+        raise ValueError(f"x must have 5 dimensions, got {tuple(x.shape)}")
+    if not isinstance(weight, torch.Tensor) or weight.dim() != 5:
+        raise ValueError("weight must be a [Cout, Cin, kt, kh, kw] tensor")
+    Cout = weight.shape[0]
     if layout == "ncthw":
         B, Cin, t, h, w = x.shape
-        n_cache = 0 if cache is None else cache.shape[2]
-        yshape = (B, weight.shape[0], t, h, w)
+        tax = 2
     else:
         B, t, h, w, Cin = x.shape
-        n_cache = 0 if cache is None else cache.shape[1]
-        yshape = (B, t, h, w, weight.shape[0])
+        tax = 1
+    n_cache = 0
+    if cache is not None:
+        if not isinstance(cache, torch.Tensor) or cache.dim() != 5 or cache.dtype != dtype:
+            raise ValueError("cache must be a 5-D tensor of x's element type")
+        n_cache = cache.shape[tax]
+        want = list(x.shape)
+        want[tax] = n_cache
+        if list(cache.shape) != want:
+            raise ValueError(f"cache has shape {tuple(cache.shape)}; with x {tuple(x.shape)} it must be {tuple(want)}")
+    yshape = (B, Cout, t, h, w) if layout == "ncthw" else (B, t, h, w, Cout)
+    if y is not None:
+        _output(y, "y", yshape, y_dtype)
+    n_out = min(2, n_cache + t)
+    cshape = list(x.shape)
+    cshape[tax] = n_out
+    if cache_out is not None:
+        _output(cache_out, "cache_out", tuple(cshape), dtype)
+    for nm, tt in (("weight", weight), ("bias", bias)):
+        if not isinstance(tt, torch.Tensor) or not tt.is_contiguous():
+            raise ValueError(f"{nm} must be a contiguous tensor")
+        dtype_code(tt.dtype)
+    _on(x, "x", device)
+    for nm, tt in (("cache", cache), ("weight", weight), ("bias", bias), ("y", y), ("cache_out", cache_out)):
+        if tt is not None:
+            _on(tt, nm, device)
+    _check_workspace(workspace, device)
+    x = x.contiguous()
+    if cache is not None:
+        cache = cache if cache_out is not None and cache_out.data_ptr() == cache.data_ptr() else cache.contiguous()
     if y is None:
-        y = torch.empty(yshape, dtype=dtype, device=x.device)
-    need = conv_workspace_size(B, Cin, weight.shape[0], t, h, w, n_cache, layout, dtype)
-    ws = _workspace(need, x.device, workspace)
+        y = torch.empty(yshape, dtype=y_dtype, device=device)
+    if cache_out is None and return_cache:
+        cache_out = torch.empty(tuple(cshape), dtype=dtype, device=device)
+    need = conv_workspace_size(B, Cin, Cout, t, h, w, n_cache, layout, dtype, y_dtype)
+    ws = _workspace(need, device, workspace)
     W, Bt = tensor_struct("weight", weight), tensor_struct("bias", bias)
     cache_ptr = None if cache is None else cache.data_ptr()
+    co_ptr = None if cache_out is None else cache_out.data_ptr()
     check(lib().wanvae_causal_conv3d(x.data_ptr(), cache_ptr, B, Cin, t, h, w, n_cache, ctypes.byref(W),
                                      ctypes.byref(Bt), _LAYOUTS[layout], dtype_code(dtype), y.data_ptr(),
-                                     ws.data_ptr(), need, _stream(x.device)))
-    return y
+                                     dtype_code(y_dtype), co_ptr, ws.data_ptr(), need, _stream(device)))
+    return (y, cache_out) if return_cache else y
 
 
 causal_conv3d = wanvae_causal_conv3d
@@ -228,19 +358,38 @@ def attn_workspace_size(B, C, T, h, w, layout, dtype) -> int:
 def wanvae_attn_block(x: torch.Tensor, gamma, qkv_w, qkv_b, proj_w, proj_b, layout: str = "ncthw",
                       y: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """The mid-block attention block on x; compute type = x.dtype."""
+    if layout not in _LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(_LAYOUTS)}, not {layout!r}")
+    device = _device_of(x, "x")
     dtype = x.dtype
+    dtype_code(dtype)
+    if x.dim() != 5:
+        raise ValueError(f"x must have 5 dimensions, got {tuple(x.shape)}")
     if layout == "ncthw":
         B, C, T, h, w = x.shape
     else:
         B, T, h, w, C = x.shape
+    if y is not None:
+        _output(y, "y", tuple(x.shape), dtype)
+    params = (("gamma", gamma), ("qkv_w", qkv_w), ("qkv_b", qkv_b), ("proj_w", proj_w), ("proj_b", proj_b))
+    for nm, tt in params:
+        if not isinstance(tt, torch.Tensor) or not tt.is_contiguous():
+            raise ValueError(f"{nm} must be a contiguous tensor")
+        dtype_code(tt.dtype)
+    _on(x, "x", device)
+    for nm, tt in params + (("y", y),):
+        if tt is not None:
+            _on(tt, nm, device)
+    _check_workspace(workspace, device)
+    x = x.contiguous()
     if y is None:
         y = torch.empty_like(x)
     need = attn_workspace_size(B, C, T, h, w, layout, dtype)
-    ws = _workspace(need, x.device, workspace)
+    ws = _workspace(need, device, workspace)
     ts = [tensor_struct(n, t) for n, t in
           (("gamma", gamma), ("qkv_w", qkv_w), ("qkv_b", qkv_b), ("proj_w", proj_w), ("proj_b", proj_b))]
     check(lib().wanvae_attn_block(x.data_ptr(), _LAYOUTS[layout], B, C, T, h, w, *[ctypes.byref(t) for t in ts],
-                                  dtype_code(dtype), y.data_ptr(), ws.data_ptr(), need, _stream(x.device)))
+                                  dtype_code(dtype), y.data_ptr(), ws.data_ptr(), need, _stream(device)))
     return y
 
 
