@@ -6,9 +6,11 @@ differences left are those of the page's "Precision" section: where the decode r
 bf16. The RMS norm (whose float32 sum of squares still differs from the oracle's float64 one in
 its last bits), the residual and DupUp3D sums, the time conv's interleave, the attention
 block's residual, unpatchify and clamp are then checked bit for bit: at least 99.9% of the
-video's values equal the oracle's, and every other one within one bf16 spacing (a norm whose
-float32 rounding lands on the other side of a bf16 rounding boundary moves one value by one
-spacing). fp32 decodes under the same weights agree with the oracle to float32 rounding.
+video's values equal the oracle's, and every other one within 2^-7, one bf16 spacing at the top
+of the video's range [-1, 1] (a norm whose float32 rounding lands on the other side of a bf16
+rounding boundary moves one value by one spacing at that value's magnitude; a sum that
+cancels to near zero keeps that absolute difference, so the bound is absolute). fp32 decodes
+under the same weights agree with the oracle to float32 rounding.
 """
 import numpy as np
 import pytest
@@ -51,7 +53,7 @@ def test_exact_sum_decode_bf16_bit_level(case):
     ulp = bf16_ulp(np.maximum(np.abs(got), np.abs(want)))
     say(case, "bit-equal", exact, "max diff", d.max(), "max diff / spacing", (d / ulp).max())
     assert exact >= 0.999, exact
-    assert np.all(d <= ulp), (d / ulp).max()
+    assert d.max() <= 2.0 ** -7, d.max()
 
 
 @pytest.mark.parametrize("case", CASES[:2])

@@ -22,6 +22,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "internal.h"
 
@@ -1309,7 +1310,27 @@ __global__ void __launch_bounds__(64 * WGC * WGP, 1) k_conv_halo(const ConvArgs 
 //
 // y = x / max(||x||_2, 1e-12) (rounded), * sqrt(C) (rounded), * gamma (rounded), then
 // optionally SiLU (rounded): the 16-bit chain of the page's "Precision" section; in fp32
-// every rounding is the float32 one. One wave per position, C <= 1024.
+// every rounding is the float32 one.
+
+// SiLU u / (1 + exp(-u)) of a bf16 value u to about one float32 ulp in a few instructions.
+// exp(-u) = 2^(-u L) e^(u (L - log2 e) ln 2) with L = log2(e) to 16 significant bits: the
+// product -u L of the 8-bit u is exact in float32, the hardware 2^x takes it, and the small
+// remainder factor is 1 + a (a = u (L - log2 e) ln 2, |a| < 1e-4 for |u| < 16). The quotient
+// comes from the hardware reciprocal with one Newton correction. Where exp(-u) overflows
+// (u < -88) the quotient is -0, the limit.
+__device__ __forceinline__ float silu_bf16(float u) {
+  constexpr float kL16 = 1.44268798828125f;      // 47274 / 2^15
+  constexpr float kRem = -4.8884954e-06f;        // (kL16 - log2 e) ln 2
+  const float E = __builtin_amdgcn_exp2f(-u * kL16);
+  const float e = __builtin_fmaf(E, u * kRem, E);
+  const float d = 1.f + e;
+  const float r = __builtin_amdgcn_rcpf(d);
+  const float q0 = u * r;
+  const float q = __builtin_fmaf(__builtin_fmaf(-q0, d, u), r, q0);
+  return d < 3.0e38f ? q : -0.f;
+}
+
+// One wave per position, C <= 1024 (the widths without a k_norm_v instance).
 template <typename T>
 __global__ void __launch_bounds__(256) k_norm(const NormArgs a) {
   using X = Elem<T>;
@@ -1323,19 +1344,21 @@ __global__ void __launch_bounds__(256) k_norm(const NormArgs a) {
   const T* x = (const T*)a.in[t] + b * a.in_bs[t] + (int64_t)pos * a.C;
   T* y = (T*)a.out[t] + b * a.out_bs[t] + (int64_t)pos * a.C;
   float v[16];
-  float ss = 0.f;
+  // the sum of squares and the normalisation in float64 for bf16 (as in k_norm_v)
+  using Acc = typename std::conditional<sizeof(T) == 2, double, float>::type;
+  Acc ss = 0;
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int c = (it * 64 + lane) * 4;
     if (c < a.C) {
       X::ld4(x + c, v + 4 * it);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ss += v[4 * it + e] * v[4 * it + e];
+      for (int e = 0; e < 4; ++e) ss += (Acc)v[4 * it + e] * (Acc)v[4 * it + e];
     }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
-  const float d = fmaxf(sqrtf(ss), 1e-12f);
+  const Acc d = ss > (Acc)1e-24 ? (Acc)sqrt(ss) : (Acc)1e-12;
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int c = (it * 64 + lane) * 4;
@@ -1343,10 +1366,10 @@ __global__ void __launch_bounds__(256) k_norm(const NormArgs a) {
       float o[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float u = X::R(v[4 * it + e] / d);
+        float u = X::R((float)((Acc)v[4 * it + e] / d));
         u = X::R(u * a.sqrtC);
         u = X::R(u * a.gamma[c + e]);
-        if (a.silu) u = X::R(u / (1.f + expf(-u)));
+        if (a.silu) u = X::R(sizeof(T) == 2 ? silu_bf16(u) : u / (1.f + expf(-u)));
         o[e] = u;
       }
       X::st4(y + c, o);
@@ -1397,7 +1420,10 @@ __global__ void __launch_bounds__(256) k_norm_v(const NormArgs a) {
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     float val[VPL][EV];
-    float ss = 0.f;
+    // bf16: the sum of squares in float64, so that ||x|| and x / ||x|| are exact to far below
+    // the bf16 rounding that follows; fp32: in float32
+    using Acc = typename std::conditional<sizeof(T) == 2, double, float>::type;
+    Acc ss = 0;
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
       if constexpr (sizeof(T) == 2) {
@@ -1407,20 +1433,26 @@ __global__ void __launch_bounds__(256) k_norm_v(const NormArgs a) {
         val[v][2] = __uint_as_float(buf[r][v].z), val[v][3] = __uint_as_float(buf[r][v].w);
       }
 #pragma unroll
-      for (int e = 0; e < EV; ++e) ss += val[v][e] * val[v][e];
+      for (int e = 0; e < EV; ++e) ss += (Acc)val[v][e] * (Acc)val[v][e];
     }
 #pragma unroll
     for (int off = LPP / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
     if (!outp[r]) continue;
-    const float d = fmaxf(sqrtf(ss), 1e-12f);
-    const float inv = 1.f / d;
+    const float d = fmaxf(sqrtf((float)ss), 1e-12f);
+    // bf16: 1 / max(||x||, 1e-12) in float64, carried as two floats ih + il
+    const double dinv = fmin(rsqrt((double)ss), 1e12);
+    const float ih = (float)dinv, il = (float)(dinv - (double)ih);
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
       const int c0 = (v * LPP + li) * EV;
       float o[EV];
       if constexpr (sizeof(T) == 2) {
-        // bf16: reciprocal multiply, hardware exp and reciprocal; each differs from the
-        // correctly rounded fp32 operation by a few fp32 ulp, below the bf16 rounding
+        // bf16: x / ||x|| as x ih + x il, rounded once (to within 2^-47 of the float64
+        // quotient, then to float32 and bf16, as a float64 value is cast to bf16); the
+        // products by sqrt(C) and gamma in float32 (exact before their rounding); SiLU to
+        // about one float32 ulp (silu_bf16). A float32 result then lands on the far side of a
+        // bf16 rounding boundary from the exact value only where it lies within about an ulp
+        // of that boundary.
         auto round2 = [](float& p, float& q) {
           const uint32_t w = pack2_bf16(p, q);
           p = __uint_as_float(w << 16);
@@ -1428,15 +1460,16 @@ __global__ void __launch_bounds__(256) k_norm_v(const NormArgs a) {
         };
 #pragma unroll
         for (int e = 0; e < EV; e += 2) {
-          float u0 = val[v][e] * inv, u1 = val[v][e + 1] * inv;
+          float u0 = __builtin_fmaf(val[v][e], ih, val[v][e] * il);
+          float u1 = __builtin_fmaf(val[v][e + 1], ih, val[v][e + 1] * il);
           round2(u0, u1);
           u0 *= a.sqrtC, u1 *= a.sqrtC;
           round2(u0, u1);
           u0 *= g[v][e], u1 *= g[v][e + 1];
           if constexpr (SILU) {
             round2(u0, u1);
-            u0 = u0 * __builtin_amdgcn_rcpf(1.f + __expf(-u0));
-            u1 = u1 * __builtin_amdgcn_rcpf(1.f + __expf(-u1));
+            u0 = silu_bf16(u0);
+            u1 = silu_bf16(u1);
           }
           o[e] = u0, o[e + 1] = u1;  // rounded by the packing store
         }
