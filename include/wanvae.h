@@ -127,6 +127,23 @@ int wanvae_causal_conv3d(const void *x, const void *cache, int64_t B, int64_t Ci
                          void *stream);
 
 /*
+ * wanvae_causal_conv3d_noalloc -- wanvae_causal_conv3d for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid it). The
+ * same conv, arguments, outputs and errors as wanvae_causal_conv3d, with its workspace in a
+ * fixed 128 MiB device array of the library (one per GPU, held until the process ends)
+ * instead of memory the call allocates or the caller brings; the call itself allocates
+ * nothing. A conv whose workspace (wanvae_causal_conv3d_workspace_size) exceeds 128 MiB ->
+ * WANVAE_EWORKSPACE before anything is launched (the 1024-channel 44 x 80 conv with two cached
+ * frames takes 114 MB channels-last; channels-first layouts also hold converted copies of x,
+ * cache and y). All calls on one GPU share its array: calls that overlap in time on one GPU
+ * race, so the caller orders them (one stream, or events).
+ */
+int wanvae_causal_conv3d_noalloc(const void *x, const void *cache, int64_t B, int64_t Cin, int64_t t,
+                                 int64_t h, int64_t w, int64_t n_cache, const wanvae_tensor *weight,
+                                 const wanvae_tensor *bias, int32_t layout, int32_t dtype, void *y,
+                                 int32_t y_dtype, void *cache_out, void *stream);
+
+/*
  * wanvae_attn_block -- the mid-block attention block (WanAttentionBlock, "The parts":
  * attention), per frame of x [B, C, T, h, w]: n = RMS norm of x over channels (times
  * sqrt(C) and gamma); q, k, v = channels [0,C), [C,2C), [2C,3C) of a 1x1 conv C -> 3C

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libwanvae.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = os.environ.get("WANVAE_ARCH", "gfx950")
-SOURCES = ["kernels.hip", "tiles.hip", "wanvae.cpp"]
+SOURCES = ["kernels.hip", "tiles.hip", "wanvae.cpp", "noalloc.hip"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
          "-packed-fp32-ops", f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}", "-Wno-unused-result"]
 

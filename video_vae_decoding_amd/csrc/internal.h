@@ -9,6 +9,8 @@
 
 #include <cstdint>
 
+#include "wanvae.h"
+
 namespace wanvae {
 
 constexpr int kMaxFrames = 8;  // 2 history frames + up to 4 chunk frames, or 8 interleaved outputs
@@ -140,5 +142,17 @@ hipError_t launch_ncthw_to_frames(const void* x, int src_dtype, void* dst, int d
 // frames [T][B][H][W][C] -> NCTHW [B][C][T][H][W], same dtype
 hipError_t launch_frames_to_ncthw(const void* x, void* dst, int dtype, int B, int C, int T, int H, int W,
                                   hipStream_t s);
+
+// The single causal conv in two halves (wanvae.cpp), for entry points that bring their own
+// device memory: conv_plan validates the arguments of wanvae_causal_conv3d and reports the
+// workspace the conv needs; conv_enqueue enqueues it on `ws` (at least that many bytes).
+int conv_plan(const void* x, const void* cache, int64_t B, int64_t Cin, int64_t t, int64_t h, int64_t w,
+              int64_t n_cache, const wanvae_tensor* weight, const wanvae_tensor* bias, int32_t layout, int32_t dtype,
+              const void* y, int32_t y_dtype, const void* cache_out, size_t* need);
+int conv_enqueue(const void* x, const void* cache, int64_t B, int64_t Cin, int64_t t, int64_t h, int64_t w,
+                 int64_t n_cache, const wanvae_tensor* weight, const wanvae_tensor* bias, int32_t layout,
+                 int32_t dtype, void* y, int32_t y_dtype, void* cache_out, void* ws, hipStream_t st);
+// sets the calling thread's wanvae_last_error() message; returns code
+int report(int code, const char* msg);
 
 }  // namespace wanvae

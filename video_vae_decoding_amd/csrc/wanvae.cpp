@@ -44,6 +44,11 @@ static int fail(int code, const char* fmt, ...) {
   return code;
 }
 
+int report(int code, const char* msg) {
+  g_err = msg;
+  return code;
+}
+
 #define HIP_TRY(expr)                                                                         \
   do {                                                                                        \
     hipError_t e_ = (expr);                                                                   \
@@ -1343,6 +1348,31 @@ static int conv_run(const void* x, const void* cache, int64_t B, int64_t Cin, in
   }
   return rc;
 }
+
+}  // extern "C"
+
+namespace wanvae {
+
+int conv_plan(const void* x, const void* cache, int64_t B, int64_t Cin, int64_t t, int64_t h, int64_t w,
+              int64_t n_cache, const wanvae_tensor* weight, const wanvae_tensor* bias, int32_t layout, int32_t dtype,
+              const void* y, int32_t y_dtype, const void* cache_out, size_t* need) {
+  g_err.clear();
+  if (int rc = conv_validate(x, cache, B, Cin, t, h, w, n_cache, weight, bias, layout, dtype, y, y_dtype, cache_out))
+    return rc;
+  const int64_t taps = weight->shape[2] * weight->shape[3] * weight->shape[4];
+  *need = conv_ws(B, Cin, weight->shape[0], taps, t, h, w, n_cache, layout, dtype, y_dtype);
+  return WANVAE_OK;
+}
+
+int conv_enqueue(const void* x, const void* cache, int64_t B, int64_t Cin, int64_t t, int64_t h, int64_t w,
+                 int64_t n_cache, const wanvae_tensor* weight, const wanvae_tensor* bias, int32_t layout,
+                 int32_t dtype, void* y, int32_t y_dtype, void* cache_out, void* ws, hipStream_t st) {
+  return conv_run(x, cache, B, Cin, t, h, w, n_cache, weight, bias, layout, dtype, y, y_dtype, cache_out, ws, st);
+}
+
+}  // namespace wanvae
+
+extern "C" {
 
 int wanvae_causal_conv3d_workspace_size(int64_t B, int64_t Cin, int64_t Cout, int64_t t, int64_t h, int64_t w,
                                         int64_t n_cache, int32_t layout, int32_t dtype, int32_t y_dtype,

@@ -62,6 +62,8 @@ def lib() -> ctypes.CDLL:
                                                           ctypes.POINTER(sz)]
         L.wanvae_causal_conv3d.argtypes = [vp, vp, i64, i64, i64, i64, i64, i64, T, T, i32, i32, vp, i32, vp, vp, sz,
                                            vp]
+        L.wanvae_causal_conv3d_noalloc.argtypes = [vp, vp, i64, i64, i64, i64, i64, i64, T, T, i32, i32, vp, i32, vp,
+                                                   vp]
         L.wanvae_attn_block_workspace_size.argtypes = [i64, i64, i64, i64, i64, i32, i32, ctypes.POINTER(sz)]
         L.wanvae_attn_block.argtypes = [vp, i32, i64, i64, i64, i64, i64, T, T, T, T, T, i32, vp, vp, sz, vp]
         L.wanvae_profile_enable.argtypes = [ctypes.c_int]
@@ -76,7 +78,7 @@ def lib() -> ctypes.CDLL:
                                                          ctypes.POINTER(sz)]
         L.wanvae_decode_tiled.argtypes = [vp, i32, i64, i64, i64, i64, T, i64, i32, i32, i32, i32, i32, vp, vp, sz, vp]
         for f in ("wanvae_decode_workspace_size", "wanvae_decode", "wanvae_causal_conv3d_workspace_size",
-                  "wanvae_causal_conv3d", "wanvae_attn_block_workspace_size", "wanvae_attn_block", "wanvae_version",
+                  "wanvae_causal_conv3d", "wanvae_causal_conv3d_noalloc", "wanvae_attn_block_workspace_size", "wanvae_attn_block", "wanvae_version",
                   "wanvae_profile_enable", "wanvae_profile_read", "wanvae_set_conv_kernel",
                   "wanvae_set_decode_pipeline", "wanvae_decode_tiled_workspace_size", "wanvae_decode_tiled"):
             getattr(L, f).restype = ctypes.c_int
@@ -347,6 +349,58 @@ def wanvae_causal_conv3d(x: torch.Tensor, cache: torch.Tensor | None, weight: to
 
 
 causal_conv3d = wanvae_causal_conv3d
+
+
+def wanvae_causal_conv3d_noalloc(x: torch.Tensor, cache: torch.Tensor | None, weight: torch.Tensor,
+                                 bias: torch.Tensor, y: torch.Tensor, layout: str = "ncthw",
+                                 cache_out: torch.Tensor | None = None) -> torch.Tensor:
+    """wanvae_causal_conv3d on the library's fixed scratch (no device allocation, neither here
+    nor in the library): x, cache, weight and bias must be contiguous, and y (of the element
+    type it is to hold) and cache_out are given by the caller. Returns y."""
+    if not isinstance(y, torch.Tensor):
+        raise ValueError("y must be given: this entry point allocates nothing")
+    for nm, tt in (("x", x), ("cache", cache)):
+        if tt is not None and (not isinstance(tt, torch.Tensor) or not tt.is_contiguous()):
+            raise ValueError(f"{nm} must be a contiguous tensor (it is not copied here)")
+    device = _device_of(x, "x")
+    dtype = x.dtype
+    dtype_code(dtype)
+    if x.dim() != 5 or not isinstance(weight, torch.Tensor) or weight.dim() != 5:
+        raise ValueError("x must be 5-D and weight [Cout, Cin, kt, kh, kw]")
+    tax = 2 if layout == "ncthw" else 1
+    if layout == "ncthw":
+        B, Cin, t, h, w = x.shape
+    elif layout == "nthwc":
+        B, t, h, w, Cin = x.shape
+    else:
+        raise ValueError(f"layout must be one of {sorted(_LAYOUTS)}, not {layout!r}")
+    n_cache = 0
+    if cache is not None:
+        want = list(x.shape)
+        want[tax] = cache.shape[tax]
+        if cache.dim() != 5 or list(cache.shape) != want or cache.dtype != dtype:
+            raise ValueError(f"cache {tuple(cache.shape)} {cache.dtype} does not match x {tuple(x.shape)} {dtype}")
+        n_cache = cache.shape[tax]
+    Cout = weight.shape[0]
+    _output(y, "y", (B, Cout, t, h, w) if layout == "ncthw" else (B, t, h, w, Cout), y.dtype)
+    dtype_code(y.dtype)
+    if cache_out is not None:
+        cshape = list(x.shape)
+        cshape[tax] = min(2, n_cache + t)
+        _output(cache_out, "cache_out", tuple(cshape), dtype)
+    for nm, tt in (("weight", weight), ("bias", bias)):
+        if not isinstance(tt, torch.Tensor) or not tt.is_contiguous():
+            raise ValueError(f"{nm} must be a contiguous tensor")
+        dtype_code(tt.dtype)
+    for nm, tt in (("x", x), ("cache", cache), ("weight", weight), ("bias", bias), ("y", y), ("cache_out", cache_out)):
+        if tt is not None:
+            _on(tt, nm, device)
+    W, Bt = tensor_struct("weight", weight), tensor_struct("bias", bias)
+    check(lib().wanvae_causal_conv3d_noalloc(x.data_ptr(), None if cache is None else cache.data_ptr(), B, Cin, t, h, w,
+                                             n_cache, ctypes.byref(W), ctypes.byref(Bt), _LAYOUTS[layout],
+                                             dtype_code(dtype), y.data_ptr(), dtype_code(y.dtype),
+                                             None if cache_out is None else cache_out.data_ptr(), _stream(device)))
+    return y
 
 
 def attn_workspace_size(B, C, T, h, w, layout, dtype) -> int:
