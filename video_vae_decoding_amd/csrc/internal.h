@@ -82,6 +82,22 @@ struct AttnArgs {
   float* ml;       // [ksplit][nfr][S][2] running max (base-2 units) and sum of each key range
 };
 
+// The bf16 attention core with the scores materialised (kernels.hip, k_attn_mm): q, k, vt as
+// for AttnArgs; p [nfr][S][Sp] bf16 (the tile-relative softmax numerators, keys in V^T's slot
+// order), ml [nfr][nkt][S] (each 128-key tile's max and sum per query), fac [nfr][nkt][S] (each
+// tile's weight per query), o [nfr][S][C]. nkt = ceil(S / 128).
+struct AttnMatArgs {
+  const void* q;
+  const void* k;
+  const void* vt;
+  void* p;
+  float2* ml;
+  float* fac;
+  void* o;
+  int nfr, S, Sp, C, nkt;
+  float sc;  // 1/sqrt(C) * log2(e)
+};
+
 // Tile shapes of the conv kernel: channels x positions per workgroup.
 enum ConvTile {
   kTile128x128 = 0,  // register-staged loads (bf16 and fp32)
@@ -130,6 +146,8 @@ hipError_t launch_conv(const ConvArgs& a, int dtype, int tile, hipStream_t s);
 bool conv_halo_supported(const ConvArgs& a, int dtype, int tile);
 hipError_t launch_norm(const NormArgs& a, int dtype, hipStream_t s);
 bool attn_supported(int C, int dtype);
+// bf16 only; C % 64 == 0, Sp a multiple of 32 >= S
+hipError_t launch_attn_mm(const AttnMatArgs& a, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, int dtype, hipStream_t s);
 // w [Cout][Cin][taps] (src dtype) -> [Cout][taps][Cin] (dst dtype), rounded to nearest even
 hipError_t launch_repack(const void* w, int src_dtype, void* dst, int dst_dtype, int Cout, int Cin, int taps,

@@ -1855,6 +1855,286 @@ __global__ void __launch_bounds__(256) k_attn_combine(const AttnArgs a) {
   X::st4((T*)a.o + row * a.C + d, v);
 }
 
+// ------------------------------------------------------------------ attention, materialised scores (bf16)
+//
+// The bf16 attention core as two NT GEMMs on MFMA with the scores in between in HBM, so that
+// neither GEMM holds a d = C wide accumulator (what limits the flash kernel above to 32
+// queries per workgroup at C = 1,024, and so makes it re-read K and V from L2 once per 32
+// queries):
+//  scores (k_attn_mm<0>): D[j][i] = K_j . Q_i for a tile of keys j x queries i of one frame
+//    (K = C). Epilogue: s = D * scale * log2(e); per query and 128-key tile t the max m_t over
+//    the tile's keys (keys past S count as -inf); p = 2^(s - m_t) rounded to bf16, stored in
+//    P[i][j] with the keys of each 32-key block in the vt_slot order of V^T; l_t = the sum of
+//    those rounded p; (m_t, l_t) stored per (query, key tile).
+//  k_attn_fac: per query, M = max_t m_t, L = sum_t l_t 2^(m_t - M) and the tile weights
+//    f_t = max(2^(m_t - M) / L, 2^-100), written as g_t = f_t / f_t+1 (the last: f_t).
+//  P V (k_attn_mm<1>): D[c][i] = sum_t f_t(i) sum_{j in tile t} V^T[c][j] P[i][j] for a tile
+//    of channels x queries (K = the frame's keys). After each key tile's products the
+//    accumulator is scaled by that tile's g: it then holds (sum_{s <= t} f_s A_s) / f_t+1,
+//    at most 2^100 times an output (no overflow), and the last scale leaves sum_t f_t A_t. A
+//    tile whose weight is clamped to 2^-100 moves O by under 2^-93 of its scale. O = D
+//    rounded to bf16 once: the softmax weights of each query sum to 1 over P's rounded values.
+// Both share the pipeline of k_conv_dma: 64-byte rows of 4 chunks (slot = chunk ^ ((row >> 1)
+// & 3)), direct-to-LDS loads four steps deep, one barrier per step. Two tile shapes: 128 x 128
+// with 4 waves of 64 x 64 and two workgroups per CU, for grids too small to fill the chip
+// with larger tiles; 256 x 256 with 8 waves of 128 x 64, half the L2 traffic and a third less
+// LDS traffic per FLOP. Rows past the end of a tensor are read from its last row and never
+// stored, so every load stays inside the tensor.
+
+template <int MODE, int BM, int BN, int WGM, int WGN>
+__global__ void __launch_bounds__(64 * WGM * WGN, WGM * WGN == 4 ? 2 : 1) k_attn_mm(const AttnMatArgs a) {
+  using T = bf16_t;
+  constexpr bool PV = MODE == 1;
+  constexpr int NW = WGM * WGN, ROWB = 64, STAGES = 4, KT = 128;
+  constexpr int TM = BM / WGM, TN = BN / WGN;  // wave tile
+  constexpr int TCN = TM / 16, TPN = TN / 16;  // its 16-row fragments
+  constexpr int SA = BM * ROWB, STAGE = (BM + BN) * ROWB;
+  constexpr int NIA = BM / (16 * NW), NIB = BN / (16 * NW);  // 16-row DMA instructions per wave and step
+  constexpr int NI = NIA + NIB;
+  constexpr int WPT = KT / TM;  // waves along M per 128-key tile (scores)
+  static_assert(NIA * 16 * NW == BM && NIB * 16 * NW == BN && (WPT == 1 || WPT == 2) && TM * WPT == KT,
+                "tile / wave split");
+  // one array per stage: the compiler then sees that the LDS reads of a step do not alias the
+  // copies in flight into the other stages
+  __shared__ __attribute__((aligned(1024))) char s0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char s1[STAGE];
+  __shared__ __attribute__((aligned(1024))) char s2[STAGE];
+  __shared__ __attribute__((aligned(1024))) char s3[STAGE];
+  char* bufs[STAGES] = {s0, s1, s2, s3};
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int S = a.S, Sp = a.Sp, C = a.C;
+  const int Mrows = PV ? C : S;  // A rows: channels (P V) or keys (scores)
+  const int nmt = (Mrows + BM - 1) / BM, nnt = (S + BN - 1) / BN;
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int fr = __builtin_amdgcn_readfirstlane(bid / (nmt * nnt));
+  const int rem = bid - fr * nmt * nnt;
+  const int nt = __builtin_amdgcn_readfirstlane(rem / nmt), mt = __builtin_amdgcn_readfirstlane(rem - nt * nmt);
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int lrow = lane >> 2, lslot = lane & 3, lchunk = lslot ^ ((lrow >> 1) & 3);
+  const int64_t ld = PV ? Sp : C;  // elements per row of A and of B
+  const T* Abase = PV ? (const T*)a.vt + (int64_t)fr * C * Sp : (const T*)a.k + (int64_t)fr * S * C;
+  const T* Bbase = PV ? (const T*)a.p + (int64_t)fr * S * Sp : (const T*)a.q + (int64_t)fr * S * C;
+  const char* asrc[NIA];
+  const char* bsrc[NIB];
+#pragma unroll
+  for (int i = 0; i < NIA; ++i) {
+    const int row = min(m0 + (wave * NIA + i) * 16 + lrow, Mrows - 1);
+    asrc[i] = (const char*)(Abase + row * ld) + lchunk * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < NIB; ++i) {
+    const int row = min(n0 + (wave * NIB + i) * 16 + lrow, S - 1);
+    bsrc[i] = (const char*)(Bbase + row * ld) + lchunk * 16;
+  }
+  const int steps = (int)(ld / 32);
+  auto issue = [&](char* b, int s) {
+    const int ko = s * ROWB;
+#pragma unroll
+    for (int i = 0; i < NIA; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(asrc[i] + ko), LDS_PTR(b + (wave * NIA + i) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < NIB; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(bsrc[i] + ko), LDS_PTR(b + SA + (wave * NIB + i) * 1024), 16, 0,
+                                       0);
+  };
+  // P V: each key tile's TPN scale loads are issued at the tile's first step, after its DMA
+  // refill; a wait for step s's loads then allows 2 * NI newer loads, plus those TPN at the
+  // three steps after a tile's first one
+  auto sync_step = [&](int s, int u) {
+    if (s + STAGES - 2 < steps) {
+      if (PV && u != 0)
+        wait_vm_lgkm0<2 * NI + TPN>();
+      else
+        wait_vm_lgkm0<2 * NI>();
+    } else {
+      wait_vm_lgkm0<0>();
+    }
+    __builtin_amdgcn_s_barrier();
+  };
+
+  f32x4_t acc[TCN][TPN];
+#pragma unroll
+  for (int ic = 0; ic < TCN; ++ic)
+#pragma unroll
+    for (int ip = 0; ip < TPN; ++ip) acc[ic][ip] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // the queries of this lane's accumulator columns
+  int qcol[TPN];
+#pragma unroll
+  for (int ip = 0; ip < TPN; ++ip) qcol[ip] = min(n0 + wn * TN + ip * 16 + (lane & 15), S - 1);
+  float gcur[TPN], gnext[TPN];
+  auto load_g = [&](float* g, int t) {
+    const int tt = min(t, a.nkt - 1);
+#pragma unroll
+    for (int ip = 0; ip < TPN; ++ip) g[ip] = a.fac[((int64_t)fr * a.nkt + tt) * S + qcol[ip]];
+  };
+  if constexpr (PV) load_g(gcur, 0);
+  const int rslot = ((lane >> 4) ^ (((lane & 15) >> 1) & 3)) * 16 + (lane & 15) * ROWB;
+#pragma unroll
+  for (int p = 0; p < STAGES - 1; ++p)
+    if (p < steps) issue(bufs[p], p);
+  // STAGES = 4 steps of 32 keys = one 128-key tile per pass
+  for (int sb = 0; sb < steps; sb += STAGES) {
+#pragma unroll
+    for (int u = 0; u < STAGES; ++u) {
+      const int s = sb + u;
+      if (s < steps) {
+        sync_step(s, u);
+        if (s + STAGES - 1 < steps) issue(bufs[(u + STAGES - 1) % STAGES], s + STAGES - 1);
+        if (PV && u == 0) load_g(gnext, sb / STAGES + 1);
+        const char* b = bufs[u];
+        uint4 af[TCN], bf[TPN];
+#pragma unroll
+        for (int ic = 0; ic < TCN; ++ic) af[ic] = *(const uint4*)(b + (wm * TM + ic * 16) * ROWB + rslot);
+#pragma unroll
+        for (int ip = 0; ip < TPN; ++ip) bf[ip] = *(const uint4*)(b + SA + (wn * TN + ip * 16) * ROWB + rslot);
+#pragma unroll
+        for (int ip = 0; ip < TPN; ++ip)
+#pragma unroll
+          for (int ic = 0; ic < TCN; ++ic) Mma<T>::run(acc[ic][ip], af[ic], bf[ip]);
+      }
+    }
+    if constexpr (PV) {
+      // the 128-key tile of these four steps is in: scale by its g
+#pragma unroll
+      for (int ip = 0; ip < TPN; ++ip) {
+#pragma unroll
+        for (int ic = 0; ic < TCN; ++ic)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[ic][ip][e] *= gcur[ip];
+        gcur[ip] = gnext[ip];
+      }
+    }
+  }
+  wait_vm_lgkm0<0>();
+
+  if constexpr (PV) {
+    // O[i][c .. c + 3], rounded once
+#pragma unroll
+    for (int ip = 0; ip < TPN; ++ip) {
+      const int i = n0 + wn * TN + ip * 16 + (lane & 15);
+      if (i >= S) continue;
+#pragma unroll
+      for (int ic = 0; ic < TCN; ++ic) {
+        const int c = m0 + wm * TM + ic * 16 + 4 * (lane >> 4);
+        if (c < C) {
+          uint2 pk;
+          pk.x = pack2_bf16(acc[ic][ip][0], acc[ic][ip][1]);
+          pk.y = pack2_bf16(acc[ic][ip][2], acc[ic][ip][3]);
+          *(uint2*)((T*)a.o + ((int64_t)fr * S + i) * C + c) = pk;
+        }
+      }
+    }
+  } else {
+    // softmax of each 128-key tile: scores in base 2, the keys past S masked. A tile is one
+    // wave's rows (WPT = 1) or those of two waves, combined through LDS (WPT = 2).
+    float* red = (float*)s0;  // [WGM][BN] per-wave maxima, then sums
+    const int jb = m0 + wm * TM + 4 * (lane >> 4);
+#pragma unroll
+    for (int ic = 0; ic < TCN; ++ic)
+#pragma unroll
+      for (int ip = 0; ip < TPN; ++ip)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[ic][ip][e] = jb + ic * 16 + e < S ? acc[ic][ip][e] * a.sc : -INFINITY;
+    float mx[TPN];
+#pragma unroll
+    for (int ip = 0; ip < TPN; ++ip) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int ic = 0; ic < TCN; ++ic)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) m = fmaxf(m, acc[ic][ip][e]);
+      m = fmaxf(m, __shfl_xor(m, 16, 64));
+      m = fmaxf(m, __shfl_xor(m, 32, 64));
+      mx[ip] = m;
+    }
+    if constexpr (WPT == 2) {
+      __syncthreads();  // every wave is done with the stage buffers
+      if ((lane >> 4) == 0) {
+#pragma unroll
+        for (int ip = 0; ip < TPN; ++ip) red[wm * BN + wn * TN + ip * 16 + lane] = mx[ip];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int ip = 0; ip < TPN; ++ip) {
+        const int q = wn * TN + ip * 16 + (lane & 15), w0 = wm & ~1;
+        mx[ip] = fmaxf(red[w0 * BN + q], red[(w0 + 1) * BN + q]);
+      }
+    }
+    float sm[TPN];
+#pragma unroll
+    for (int ip = 0; ip < TPN; ++ip) {
+      const int i = n0 + wn * TN + ip * 16 + (lane & 15);
+      float l = 0.f;
+#pragma unroll
+      for (int ic = 0; ic < TCN; ++ic) {
+        const float p0 = __builtin_amdgcn_exp2f(acc[ic][ip][0] - mx[ip]);
+        const float p1 = __builtin_amdgcn_exp2f(acc[ic][ip][1] - mx[ip]);
+        const float p2 = __builtin_amdgcn_exp2f(acc[ic][ip][2] - mx[ip]);
+        const float p3 = __builtin_amdgcn_exp2f(acc[ic][ip][3] - mx[ip]);
+        uint2 pk;
+        pk.x = pack2_bf16(p0, p1);
+        pk.y = pack2_bf16(p2, p3);
+        l += __uint_as_float(pk.x << 16) + __uint_as_float(pk.x & 0xffff0000u) + __uint_as_float(pk.y << 16) +
+             __uint_as_float(pk.y & 0xffff0000u);
+        const int j = jb + ic * 16;  // 4 keys j .. j + 3: consecutive slots of V^T's order
+        if (i < S && j < Sp) *(uint2*)((T*)a.p + ((int64_t)fr * S + i) * Sp + vt_slot(j)) = pk;
+      }
+      l += __shfl_xor(l, 16, 64);
+      l += __shfl_xor(l, 32, 64);
+      sm[ip] = l;
+    }
+    if constexpr (WPT == 2) {
+      __syncthreads();
+      if ((lane >> 4) == 0) {
+#pragma unroll
+        for (int ip = 0; ip < TPN; ++ip) red[wm * BN + wn * TN + ip * 16 + lane] = sm[ip];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int ip = 0; ip < TPN; ++ip) {
+        const int q = wn * TN + ip * 16 + (lane & 15), w0 = wm & ~1;
+        sm[ip] = red[w0 * BN + q] + red[(w0 + 1) * BN + q];
+      }
+    }
+    // (m_t, l_t) of this wave's 128-key tile (with WPT = 2, the even wave of the pair stores)
+    const int t = (m0 + wm * TM) / KT;
+    if ((WPT == 1 || (wm & 1) == 0) && (lane >> 4) == 0) {
+#pragma unroll
+      for (int ip = 0; ip < TPN; ++ip) {
+        const int i = n0 + wn * TN + ip * 16 + lane;
+        if (i < S && t < a.nkt) a.ml[((int64_t)fr * a.nkt + t) * S + i] = make_float2(mx[ip], sm[ip]);
+      }
+    }
+  }
+}
+
+// Per query: M = max_t m_t, L = sum_t l_t 2^(m_t - M), f_t = max(2^(m_t - M) / L, 2^-100),
+// stored as the P V kernel's scales g_t = f_t / f_t+1 and, for the last tile, f_t.
+__global__ void __launch_bounds__(256) k_attn_fac(const AttnMatArgs a) {
+  const int64_t n = (int64_t)a.nfr * a.S;
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (u >= n) return;
+  const int64_t fr = u / a.S, i = u - fr * a.S;
+  const float2* ml = a.ml + fr * a.nkt * a.S + i;
+  float M = -INFINITY;
+  for (int t = 0; t < a.nkt; ++t) M = fmaxf(M, ml[(int64_t)t * a.S].x);
+  float L = 0.f;
+  for (int t = 0; t < a.nkt; ++t) L += ml[(int64_t)t * a.S].y * exp2f(ml[(int64_t)t * a.S].x - M);
+  const float inv = 1.f / L, fmin_ = 0x1p-100f;
+  float* g = a.fac + fr * a.nkt * a.S + i;
+  float f = fmaxf(exp2f(ml[0].x - M) * inv, fmin_);
+  for (int t = 0; t + 1 < a.nkt; ++t) {
+    const float fn = fmaxf(exp2f(ml[(int64_t)(t + 1) * a.S].x - M) * inv, fmin_);
+    g[(int64_t)t * a.S] = f / fn;
+    f = fn;
+  }
+  g[(int64_t)(a.nkt - 1) * a.S] = f;
+}
+
 // ------------------------------------------------------------------ small kernels
 
 template <typename S>
@@ -2118,6 +2398,28 @@ hipError_t launch_attn(const AttnArgs& a, int dtype, hipStream_t s) {
     }
   }
   return hipErrorInvalidValue;
+}
+
+// A tile shape's workgroups for one of the two GEMMs: the 256 x 256 tiles where they give
+// the chip at least two rounds of workgroups (one per CU), else 128 x 128 (two per CU).
+hipError_t launch_attn_mm(const AttnMatArgs& a, hipStream_t s) {
+  if (a.C % 64 != 0 || a.Sp % 32 != 0 || a.Sp < a.S || a.nkt != (a.S + 127) / 128) return hipErrorInvalidValue;
+  auto blocks = [&](int64_t rows, int tile) { return (int64_t)a.nfr * ((rows + tile - 1) / tile) * ((a.S + tile - 1) / tile); };
+  const int64_t s256 = blocks(a.S, 256), p256 = blocks(a.C, 256);
+  if (blocks(a.S, 128) >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  if (s256 >= 512)
+    hipLaunchKernelGGL((k_attn_mm<0, 256, 256, 2, 4>), dim3((unsigned)s256), dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_attn_mm<0, 128, 128, 2, 2>), dim3((unsigned)blocks(a.S, 128)), dim3(256), 0, s, a);
+  if (hipError_t e = hipGetLastError()) return e;
+  const int64_t n = (int64_t)a.nfr * a.S;
+  hipLaunchKernelGGL(k_attn_fac, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+  if (hipError_t e = hipGetLastError()) return e;
+  if (p256 >= 512)
+    hipLaunchKernelGGL((k_attn_mm<1, 256, 256, 2, 4>), dim3((unsigned)p256), dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_attn_mm<1, 128, 128, 2, 2>), dim3((unsigned)blocks(a.C, 128)), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_repack(const void* w, int src_dtype, void* dst, int dst_dtype, int Cout, int Cin, int taps,

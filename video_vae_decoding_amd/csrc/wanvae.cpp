@@ -518,7 +518,10 @@ static int run_norm(const FrameRef& in, const FrameRef& out, int F, int B, int H
 }
 
 // Attention block on nfr independent frames folded into the batch (F = 1, B = nfr):
-// n = RMS norm (no SiLU) -> 1x1 conv to q, k, v^T -> flash attention -> 1x1 proj + x.
+// n = RMS norm (no SiLU) -> 1x1 conv to q, k, v^T -> attention core -> 1x1 proj + x. The
+// bf16 core runs on the materialised-score kernels (k_attn_mm: scores GEMM with the tile
+// softmax, per-tile weights, P V GEMM); fp32 (and bf16 with WANVAE_ATTN_FLASH=1, for
+// comparison) on the flash kernel.
 struct AttnBufs {
   void *n = nullptr, *q = nullptr, *k = nullptr, *vt = nullptr, *o = nullptr;
   int S = 0, Sp = 0;
@@ -526,7 +529,17 @@ struct AttnBufs {
   int ksplit = 1;  // attention key ranges, and their partial results
   float* opart = nullptr;
   float* ml = nullptr;
+  bool mm = false;  // materialised scores: P, each key tile's (max, sum) and weight per query
+  void* p = nullptr;
+  float2* tml = nullptr;
+  float* fac = nullptr;
+  int nkt = 0;
 };
+
+static const bool g_attn_flash = [] {
+  const char* e = getenv("WANVAE_ATTN_FLASH");
+  return e && atoi(e) != 0;
+}();
 
 // Attention key ranges: with fewer than 256 workgroups of 32 queries, up to 4 ranges of keys
 // run as separate workgroups (the frames of one chunk would leave most of the chip idle).
@@ -546,6 +559,15 @@ static void plan_attn_bufs(Arena& ar, AttnBufs& ab, int nfr, int S, int C, int d
   ab.vt = ar.take((size_t)nfr * C * ab.Sp * es);
   ab.o = ar.take((size_t)nfr * S * C * es);
   if (with_split) ab.split = take_split(ar, (int64_t)nfr * S, 3 * (int64_t)C);
+  ab.mm = dtype == kBF16 && !g_attn_flash;
+  if (ab.mm) {
+    ab.nkt = (S + 127) / 128;
+    ab.p = ar.take((size_t)nfr * S * ab.Sp * es);
+    ab.tml = (float2*)ar.take((size_t)nfr * ab.nkt * S * sizeof(float2));
+    ab.fac = (float*)ar.take((size_t)nfr * ab.nkt * S * sizeof(float));
+    ab.ksplit = 1;
+    return;
+  }
   ab.ksplit = attn_split(nfr, S);
   if (ab.ksplit > 1) {
     ab.opart = (float*)ar.take((size_t)ab.ksplit * nfr * S * C * 4);
@@ -568,13 +590,22 @@ static int run_attn(const FrameRef& x, const FrameRef& y, int nfr, int H, int W,
     cc.a.S = S, cc.a.Sp = ab.Sp;
     if (int rc = run_conv(qkv, n, nfr, H, W, H, W, 1, false, cc, dtype, st)) return rc;
   }
-  AttnArgs aa;
-  aa.q = ab.q, aa.k = ab.k, aa.vt = ab.vt, aa.o = ab.o;
-  aa.nfr = nfr, aa.S = S, aa.Sp = ab.Sp, aa.C = C;
-  aa.scale = (float)(1.0 / std::sqrt((double)C));
-  aa.ksplit = ab.ksplit, aa.opart = ab.opart, aa.ml = ab.ml;
   hipEvent_t e0 = prof_start(st);
-  HIP_TRY(launch_attn(aa, dtype, st));
+  if (ab.mm) {
+    AttnMatArgs am;
+    am.q = ab.q, am.k = ab.k, am.vt = ab.vt, am.o = ab.o;
+    am.p = ab.p, am.ml = ab.tml, am.fac = ab.fac;
+    am.nfr = nfr, am.S = S, am.Sp = ab.Sp, am.C = C, am.nkt = ab.nkt;
+    am.sc = (float)(1.4426950408889634 / std::sqrt((double)C));
+    HIP_TRY(launch_attn_mm(am, st));
+  } else {
+    AttnArgs aa;
+    aa.q = ab.q, aa.k = ab.k, aa.vt = ab.vt, aa.o = ab.o;
+    aa.nfr = nfr, aa.S = S, aa.Sp = ab.Sp, aa.C = C;
+    aa.scale = (float)(1.0 / std::sqrt((double)C));
+    aa.ksplit = ab.ksplit, aa.opart = ab.opart, aa.ml = ab.ml;
+    HIP_TRY(launch_attn(aa, dtype, st));
+  }
   prof_stop(e0, WANVAE_KATTN, 4.0 * nfr * (double)S * S * C, 0, st);
   {
     ConvCall cc;
