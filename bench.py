@@ -63,26 +63,29 @@ def _cpu_model():
 def _blas():
     """The BLAS libraries behind the oracle's products (torch.mm for the convs, numpy for the
     attention) and their thread counts."""
+    import re
+
     import torch
     cfg = torch.__config__.show()
-    tb = [l.strip() for l in cfg.splitlines() if "BLAS_INFO" in l or "LAPACK_INFO" in l]
+    tb = re.findall(r"(?:BLAS_INFO|LAPACK_INFO)=[^,\s]+", cfg)
     try:
         info = np.show_config(mode="dicts")
         nb = info.get("Build Dependencies", {}).get("blas", {}).get("name", "unknown")
     except Exception:  # noqa: BLE001
         nb = "unknown"
-    return {"torch": "; ".join(tb) or "unknown", "torch_threads": torch.get_num_threads(), "numpy": nb}
+    return {"torch": ", ".join(tb) or "unknown", "torch_threads": torch.get_num_threads(), "numpy": nb}
 
 
 def cpu_baseline(cfg, W, mode="bf16", chunks=3):
     """The CPU oracle as it stands (float64 sums, the mode's rounding points) decoding a causal
     prefix of the workload: latent frames 0..chunks-1 (chunk 0, chunk 1, and steady-state chunks
-    with two frames of history) of batch element 0, on a crop of the latent with 1/16 of the frame
-    area. Measured: each chunk's seconds. Extrapolated, and labelled so: the full decode's time
-    as 16 x (t0 + t1 + (T - 2) x t_steady) (conv work scales with the area; the attention, which
-    scales with its square, is under 0.2% of the work) and its frames/s."""
+    with two frames of history) of batch element 0, on a crop of the latent with 1/32 of the frame
+    area (about 20 s on 16 host cores). Measured: each chunk's seconds. Extrapolated, and
+    labelled so: the full decode's time as 32 x (t0 + t1 + (T - 2) x t_steady) (conv work scales
+    with the area; the attention, which scales with its square, is under 0.2% of the work) and
+    its frames/s."""
     import oracle
-    ch, cw = (11, 20) if cfg.h <= cfg.w else (20, 11)
+    ch, cw = (11, 10) if cfg.h <= cfg.w else (10, 11)
     z = np.ascontiguousarray(cfg.latents()[:1, :, :chunks, :ch, :cw])
     marks = []
     t0 = time.perf_counter()

@@ -1386,6 +1386,8 @@ __global__ void __launch_bounds__(256) k_norm_v(const NormArgs a) {
   using X = Elem<T>;
   constexpr int EV = 16 / (int)sizeof(T);  // elements per 16-byte vector
   constexpr int PPW = 64 / LPP;
+  constexpr int CC = LPP * VPL * EV;  // channels of a position
+  constexpr bool kSqrtPow2 = CC == 16 || CC == 64 || CC == 256 || CC == 1024;
   // grid: x = position blocks within a frame, y = (frame t, batch b)
   const int lane = threadIdx.x & 63, li = lane % LPP;
   const int t = blockIdx.y / a.B, b = blockIdx.y % a.B;
@@ -1464,7 +1466,9 @@ __global__ void __launch_bounds__(256) k_norm_v(const NormArgs a) {
           float u1 = __builtin_fmaf(val[v][e + 1], ih, val[v][e + 1] * il);
           round2(u0, u1);
           u0 *= a.sqrtC, u1 *= a.sqrtC;
-          round2(u0, u1);
+          // C = 16, 64, 256, 1024: sqrt(C) is a power of two, the product exact, its rounding
+          // the identity
+          if constexpr (!kSqrtPow2) round2(u0, u1);
           u0 *= g[v][e], u1 *= g[v][e + 1];
           if constexpr (SILU) {
             round2(u0, u1);
