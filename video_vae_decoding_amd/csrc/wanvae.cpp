@@ -411,8 +411,21 @@ static SplitBuf take_split(Arena& ar, int64_t M, int64_t Cout) {
   return b;
 }
 
+// Compute units of the current device (256 on an MI355X), looked up once per process.
+static int64_t cu_count() {
+  static const int64_t n = [] {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    return (int64_t)v;
+  }();
+  return n;
+}
+
 // K split of a direct-to-LDS conv: enough workgroups for about three per CU when the tiles
-// alone leave the chip short, at least 16 K steps per range, within the partials scratch.
+// alone leave the chip short, at least 16 K steps per range, within the partials scratch. The
+// halo tile (one workgroup per CU) takes the split that its time estimate favours.
 static int split_for(const ConvArgs& a, int tile, int dtype, const SplitBuf& sb) {
   int TC = 0, TP = 0, TPY = 0, TPX = 0;
   switch (tile) {
@@ -440,7 +453,23 @@ static int split_for(const ConvArgs& a, int tile, int dtype, const SplitBuf& sb)
     units = a.kt * a.kh * a.kw * ((a.Cin + 31) / 32) / 16;
   }
   if (tiles >= 512) return 1;
-  int ks = (int)std::min<int64_t>({4, (768 + tiles - 1) / tiles, units});
+  int ks;
+  if (TPX) {
+    // halo tile, one workgroup per CU: the split with the least estimated time, rounds of
+    // workgroups over the CUs x (the range's steps + the tile's fixed cost, about 16.5 us:
+    // 46 steps of a 16 x 16 block, 23 of a 512-position block)
+    const int64_t steps = (int64_t)a.kt * 9 * (a.Cin / 32), fixed = TPX * TPY == 256 ? 46 : 23;
+    const int64_t ncu = cu_count();
+    int64_t best = -1;
+    ks = 1;
+    for (int k = 1; k <= std::min<int64_t>(4, std::max<int64_t>(units, 1)); ++k) {
+      if ((size_t)k * M * a.Cout > sb.floats) break;
+      const int64_t t = (tiles * k + ncu - 1) / ncu * (steps / k + fixed);
+      if (best < 0 || t < best) best = t, ks = k;
+    }
+    return ks;
+  }
+  ks = (int)std::min<int64_t>({4, (768 + tiles - 1) / tiles, units});
   while (ks > 1 && (size_t)ks * M * a.Cout > sb.floats) --ks;
   return std::max(ks, 1);
 }
