@@ -950,6 +950,41 @@ __device__ __forceinline__ void buffer_lds16(const char* base, uint32_t bytes, c
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LDS_PTR(lds), 16, voff, soff, 0, 0);
 }
 
+// Patch row (relative to a wave's first) that tile row k reads at tap row dy: the same row
+// shifted by dy, or, for the 2x upsampled input, the source row of the nearest neighbour.
+template <bool UP>
+__host__ __device__ constexpr int halo_rowc(int k, int dy) {
+  return UP ? ((k + dy - 1) >> 1) + 1 : k + dy;
+}
+// The first tap row that reads patch row q (3: none) with RW tile rows per wave.
+template <bool UP, int RW>
+__host__ __device__ constexpr int halo_first_dy(int q) {
+  for (int dy = 0; dy < 3; ++dy)
+    for (int k = 0; k < RW; ++k)
+      if (halo_rowc<UP>(k, dy) == q) return dy;
+  return 3;
+}
+// How many patch rows are first read at tap row dy.
+template <bool UP, int RW>
+__host__ __device__ constexpr int rows_first_used(int dy) {
+  int n = 0;
+  for (int q = 0; q < (UP ? RW / 2 + 2 : RW + 2); ++q) n += halo_first_dy<UP, RW>(q) == dy ? 1 : 0;
+  return n;
+}
+// Interleaves a step's NRD LDS reads with its NMF MFMAs: one read, then MPR MFMAs, the reads
+// early in the step (two MFMAs each, the rest after them) so that they have landed by its
+// end: 1-3% faster than spread over the whole step, and 3% faster than all reads first.
+template <int NRD, int NMF>
+__device__ __forceinline__ void interleave_reads() {
+  constexpr int MPR = NMF >= 2 * NRD ? 2 : (NMF + NRD - 1) / NRD;
+#pragma unroll
+  for (int r = 0; r < NRD; ++r) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, MPR, 0);
+  }
+  if constexpr (NMF > MPR * NRD) __builtin_amdgcn_sched_group_barrier(0x008, NMF - MPR * NRD, 0);
+}
+
 template <int TC, int TPY, int TPX, int WGC, int WGP, bool UP>
 __global__ void __launch_bounds__(64 * WGC * WGP, 1) k_conv_halo(const ConvArgs a) {
   using T = bf16_t;
@@ -1059,8 +1094,9 @@ __global__ void __launch_bounds__(64 * WGC * WGP, 1) k_conv_halo(const ConvArgs 
   // byte offset). Groups advance without divisions: channel block minor, time tap major.
   // a step past the last loads zeros (an empty descriptor): every wave issues the same loads
   // at every step, so the wait counts below are constants
+  // step j of a group takes tap (dy, dx) = (j % 3, j / 3), stored at tap index 3 dy + dx
   auto issue_w = [&](char* buf, int wofs, int j, bool valid) {
-    const int so = wofs + j * Cin * 2;
+    const int so = wofs + ((j % 3) * 3 + j / 3) * Cin * 2;
     const uint32_t nb = valid && !(WSPARE && wave > 0) ? wbytes : 0u;
 #pragma unroll
     for (int i = 0; i < NIW; ++i) buffer_lds16(wbase, nb, buf + wdst(i), woffl[i], so);
@@ -1112,25 +1148,33 @@ __global__ void __launch_bounds__(64 * WGC * WGP, 1) k_conv_halo(const ConvArgs 
       pvb[xg][dx] = (wrow * PW + col) * 64 + (((lane >> 4) ^ ((col >> 1) & 3)) << 4);
     }
 
-  // two register sets of fragments: step s computes from set s & 1 while step s + 1's
-  // fragments are read into the other
-  uint4 wf[2][TCN], bf[2][TPN];
-  auto read_frags = [&](int set, const char* wbuf, const char* pbuf, int j) {
-    const int dy = j / 3, dx = j % 3;
+  // Taps run dx-major: step j of a group is tap (dy, dx) = (j % 3, j / 3), so the three steps
+  // of one column shift dx read the same patch rows shifted by one row each. A patch row's
+  // fragments are read once per dx and kept in registers for every dy that uses them: tile row
+  // k with tap dy reads patch row rowc(k, dy), so a column shift reads the RW + 2 rows
+  // (RW / 2 + 2 upsampled) once instead of 3 RW times. The rows the first step of a column
+  // shift needs are read during the last step of the one before; the rest one step before
+  // their first use. Weight fragments: two register sets, step s computes from set s & 1
+  // while step s + 1's are read into the other.
+  constexpr int NQ = UP ? RW / 2 + 2 : RW + 2;  // patch rows a column shift reads
+  uint4 wf[2][TCN], bc[NQ][NXG];
+  auto read_w = [&](int set, const char* wbuf) {
 #pragma unroll
     for (int ic = 0; ic < TCN; ++ic) wf[set][ic] = *(const uint4*)(wbuf + wrd + ic * 16 * 64);
-#pragma unroll
-    for (int ip = 0; ip < TPN; ++ip) {
-      const int k = (ip * 16) / TPX, xg = ((ip * 16) % TPX) / 16;
-      const int rowc = UP ? ((k + dy - 1) >> 1) + 1 : k + dy;
-      bf[set][ip] = *(const uint4*)(pbuf + pvb[xg][dx] + rowc * PW * 64);
-    }
   };
-  auto mfma_all = [&](int set) {
+  // the rows q of column shift dx whose first use is at tap row dy0
+  auto read_rows = [&](const char* pbuf, int dx, int dy0) {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+      if (halo_first_dy<UP, RW>(q) == dy0)
+#pragma unroll
+        for (int xg = 0; xg < NXG; ++xg) bc[q][xg] = *(const uint4*)(pbuf + pvb[xg][dx] + q * PW * 64);
+  };
+  auto mfma_all = [&](int set, int dy) {
 #pragma unroll
     for (int ip = 0; ip < TPN; ++ip)
 #pragma unroll
-      for (int ic = 0; ic < TCN; ++ic) Mma<T>::run(acc[ic][ip], wf[set][ic], bf[set][ip]);
+      for (int ic = 0; ic < TCN; ++ic) Mma<T>::run(acc[ic][ip], wf[set][ic], bc[halo_rowc<UP>(ip / NXG, dy)][ip % NXG]);
   };
   // waits until this wave's loads of step x (and, at a group's first step, the group's patch,
   // issued before them) have landed and its LDS reads have returned, then the barrier. After
@@ -1148,8 +1192,8 @@ __global__ void __launch_bounds__(64 * WGC * WGP, 1) k_conv_halo(const ConvArgs 
   // x - 8; the patch of group g + 1 goes to the other patch buffer at the barrier of the
   // group's first step. Step s begins with the barrier of step s + 1: step s's fragments are
   // already in registers, so no wave reads step s's weight buffer nor the previous group's
-  // patch any more, and step s + 1's fragments are read into the other register set between
-  // step s's MFMAs.
+  // patch any more (the last step of a group reads only the next group's patch), and step
+  // s + 1's weight fragments are read into the other register set between step s's MFMAs.
   char* wb[9] = {w0, w1, w2, w3, w4, w5, w6, w7, w8};
   const int wofs0 = (dt0 * 9 * Cin + cb0) * 2;
   issue_p(p0, frame_of(dt0), cb0 * 2);
@@ -1159,7 +1203,8 @@ __global__ void __launch_bounds__(64 * WGC * WGP, 1) k_conv_halo(const ConvArgs 
   issue_w(wb[8], wofs0, 8, true);
   issue_p(p1, frame_of(dt1), cb1 * 2);
   __builtin_amdgcn_sched_barrier(0);
-  read_frags(0, wb[0], p0, 0);
+  read_w(0, wb[0]);
+  read_rows(p0, 0, 0);
 
   int wofs1 = (dt1 * 9 * Cin + cb1) * 2;  // weight offset of the next group
   for (int g0 = 0; g0 < G; g0 += 2) {
@@ -1169,30 +1214,33 @@ __global__ void __launch_bounds__(64 * WGC * WGP, 1) k_conv_halo(const ConvArgs 
       if (g < G) {
         char* pcur = gg == 0 ? p0 : p1;
         char* pnext = gg == 0 ? p1 : p0;
-        // the last step of all reads a finished buffer into the set it leaves unused, so that
+        // the last step of all reads finished buffers into registers it leaves unused, so that
         // every step is the same straight-line code
 #pragma unroll
         for (int j = 0; j < 9; ++j) {
           const int s = 9 * g + j;
           const int set = (9 * gg + j) & 1;
           const int jn = (j + 1) % 9;
+          const int dy = j % 3, dx = j / 3;
           sync_step(jn);
           issue_w(wb[j], wofs1, j, s + 9 < S);
           if (j == 8) issue_p(pcur, fb2p, cb2 * 2);
           __builtin_amdgcn_sched_barrier(0);
-          read_frags(set ^ 1, wb[jn], j == 8 ? pnext : pcur, jn);
-          mfma_all(set);
-          // one LDS read between groups of MFMAs, the reads early in the step (two MFMAs each,
-          // the rest after them) so that they have landed by its end: 1-3% faster than spread
-          // over the whole step, and 3% faster than all reads first
-          constexpr int NRD = TCN + TPN, NMF = TCN * TPN;
-          constexpr int MPR = NMF >= 2 * NRD ? 2 : (NMF + NRD - 1) / NRD;
-#pragma unroll
-          for (int r = 0; r < NRD; ++r) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, MPR, 0);
-          }
-          if constexpr (NMF > MPR * NRD) __builtin_amdgcn_sched_group_barrier(0x008, NMF - MPR * NRD, 0);
+          read_w(set ^ 1, wb[jn]);
+          mfma_all(set, dy);
+          // the patch rows whose first use is the next step: after a column shift's last tap
+          // row, the next shift's first rows (from the next group's patch after step 8)
+          if (dy == 2)
+            read_rows(j == 8 ? pnext : pcur, jn / 3, 0);
+          else
+            read_rows(pcur, dx, dy + 1);
+          // one LDS read between groups of MFMAs, the reads early in the step
+          if (dy == 2)
+            interleave_reads<TCN + NXG * rows_first_used<UP, RW>(0), TCN * TPN>();
+          else if (dy == 0)
+            interleave_reads<TCN + NXG * rows_first_used<UP, RW>(1), TCN * TPN>();
+          else
+            interleave_reads<TCN + NXG * rows_first_used<UP, RW>(2), TCN * TPN>();
           __builtin_amdgcn_sched_barrier(0);
         }
         // the cursors move one group on
