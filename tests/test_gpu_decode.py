@@ -6,8 +6,9 @@ section). A bf16 decode is more sensitive than that to the order of its float32 
 tiny decoder and at full size alike: the oracle's own bf16 decode with float64 and with float32
 sums differs by max 0.029-0.043 (mean 0.004, PSNR 50 dB). So the bf16 max and mean bound is
 1.5x that self-difference (stored for the full-size workloads), with PSNR >= 40 dB. The tiny decoder is compared in full; the full-size 704x1280 and 1280x704 decodes
-on stored oracle samples of their first 5 frames (tests/golden, made by make_golden.py from
-the oracle) and by properties that hold at any size: causality (the first 4k - 3 frames are
+on stored oracle samples of their first frames (tests/golden, made by make_golden.py from
+the oracle: 13 frames, two chunks of them in the steady state, for the 704x1280 bf16 and fp32
+decodes; 5 for the others) and by properties that hold at any size: causality (the first 4k - 3 frames are
 the decode of the first k latent frames) and determinism, bit for bit.
 """
 import json
