@@ -265,7 +265,8 @@ def single_op(name, args):
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(elapsed / args.steps * 1e3, 3),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": config,
-           "roofline": {"bound": "mfma", "kernel": "conv" if kind == "conv" else "attention core (k_attn)",
+           "roofline": {"bound": "mfma", "kernel": "conv" if kind == "conv" else (
+               "attention core (bf16: k_attn_mm scores, k_attn_fac, k_attn_mm P V; fp32: k_attn)"),
                         "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
                         "launches": main_k["launches"], "avg_launch_ms": round(main_k["ms"] / max(1, main_k["launches"]), 4)},
