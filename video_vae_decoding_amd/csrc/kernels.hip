@@ -2,7 +2,9 @@
 //
 //  k_conv_halo  bf16 3x3 causal convs (3x3x3 and the upsampling 3x3): a workgroup copies the
 //               input patch under its block of positions into LDS once per (time tap,
-//               channel block) and the nine spatial taps read shifted windows of it.
+//               channel block) and the nine spatial taps read shifted windows of it; the taps
+//               run column shift by column shift, so a wave reads each patch row once per
+//               shift and keeps it in registers for the three tap rows that use it.
 //  k_conv_dma   implicit-GEMM conv with tiles copied straight to LDS: in bf16 the other
 //               shapes (1x1 shortcuts, 3x1x1 time convs, conv_in, the attention's 1x1 convs),
 //               in fp32 every conv with more than 64 output channels.
@@ -11,11 +13,16 @@
 //               v_mfma_f32_16x16x4f32 in fp32) and fuse the epilogues: bias, residual add,
 //               DupUp3D add, the time conv's channel->frame interleave, unpatchify + clamp,
 //               and the q/k/v split.
-//  k_norm_v     WanRMS_norm (+ SiLU) per position, HBM bound.
-//  k_attn       single-head attention over the h*w positions of a frame, flash style: the
-//               head dim is split across the waves of a workgroup, partial scores are summed
-//               through LDS in a fixed order, online softmax (per wave over the whole tile,
-//               or per wave over its own query rows with P shared through LDS).
+//  k_norm_v     WanRMS_norm (+ SiLU) per position; the bf16 chain is evaluated to about a
+//               float32 ulp before each bf16 rounding, which leaves it VALU-issue bound just
+//               ahead of HBM.
+//  k_attn_mm    bf16 single-head attention over the h*w positions of a frame on materialised
+//  k_attn_fac   scores: the scores GEMM with each 128-key tile's softmax in its epilogue (P
+//               stored in bf16), the per-tile weights, and the P V GEMM with a running rescale.
+//  k_attn       the fp32 attention, flash style: the head dim is split across the waves of a
+//               workgroup, partial scores are summed through LDS in a fixed order, online
+//               softmax (per wave over the whole tile, or per wave over its own query rows
+//               with P shared through LDS).
 // The tiled decode's crop and blend kernels are in tiles.hip.
 // Reference for what is computed: FastVideo's "wan22_vae_decode reference.py" page
 // (sections "The parts" and "Precision").
