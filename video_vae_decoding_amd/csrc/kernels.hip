@@ -1312,9 +1312,32 @@ __global__ void __launch_bounds__(64 * WGC * WGP, 1) k_conv_halo(const ConvArgs 
   static_assert(NT % UPR == 0, "units per row divide the workgroup");
   constexpr int PSTEP = NT / UPR;
   const int cu = tid % UPR;
+  // The residual unit that each 8-channel store adds is copied ahead into the idle weight
+  // buffers (unit it of thread tid at buffer it, byte 16 tid; direct-to-LDS loads, one batch
+  // per pass issued before the staging) rather than loaded by each store in turn: on the
+  // level-3 residual convs 3% faster. (The same for the DupUp3D source was 1% slower.)
+  constexpr int NIT = TC == 16 ? 1 : (TP / 2) / PSTEP;
+  // (not compiled into the upsampling instances, whose convs add a DupUp3D sum, no residual)
+  constexpr bool XPRE = !UP && TC != 16 && NIT <= 9 && NT * 16 <= WBUF;
+  static_assert(TC == 16 || NIT * PSTEP == TP / 2, "units per pass divide the threads");
+  const bool xres = XPRE && a.mode == kEpiFrames && a.has_res && !a.has_dup;
+  char* const wbl[9] = {w0, w1, w2, w3, w4, w5, w6, w7, w8};
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     __syncthreads();
+    if constexpr (XPRE) {
+      if (xres) {
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+          const int p = h * (TP / 2) + tid / UPR + it * PSTEP;
+          const int y = Y0 + p / TPX, x = X0 + p % TPX;
+          const T* src = y < a.Ho && x < a.Wo
+                             ? (const T*)a.res[t] + b * a.res_bs[t] + ((int64_t)y * a.Wo + x) * a.outC + c0 + cu * 8
+                             : (const T*)g_zero_page;
+          __builtin_amdgcn_global_load_lds((const void*)src, LDS_PTR(wbl[it] + wave * 1024), 16, 0, 0);
+        }
+      }
+    }
     if (wp / (WGP / 2) == h) {
 #pragma unroll
       for (int ip = 0; ip < TPN; ++ip) {
@@ -1330,6 +1353,9 @@ __global__ void __launch_bounds__(64 * WGC * WGP, 1) k_conv_halo(const ConvArgs 
         }
       }
     }
+    if constexpr (XPRE) {
+      if (xres) wait_vm_lgkm0<0>();  // this wave's copies of the pass have landed
+    }
     __syncthreads();
     if constexpr (TC == 16) {
       // conv_out: unpatchify + clamp, 4 channels per unit (Cout is not a multiple of 8 here)
@@ -1342,6 +1368,24 @@ __global__ void __launch_bounds__(64 * WGC * WGP, 1) k_conv_halo(const ConvArgs 
           const uint2 w2 = *(const uint2*)(crow(r) + ((cu4 ^ (r & SWZ)) << 3));
           float v[4] = {bf2f(w2.x & 0xffff), bf2f(w2.x >> 16), bf2f(w2.y & 0xffff), bf2f(w2.y >> 16)};
           conv_epilogue<T>(a, t, b, y, x, c, v);
+        }
+      }
+    } else if (XPRE && xres) {
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int r = tid / UPR + it * PSTEP;
+        const int p = h * (TP / 2) + r;
+        const int y = Y0 + p / TPX, x = X0 + p % TPX;
+        if (y < a.Ho && x < a.Wo) {
+          const char* row = crow(r);
+          const uint2 lo = *(const uint2*)(row + (((2 * cu) ^ (r & SWZ)) << 3));
+          const uint2 hi = *(const uint2*)(row + (((2 * cu + 1) ^ (r & SWZ)) << 3));
+          float v[8], r8[8];
+          unpack8_bf16(make_uint4(lo.x, lo.y, hi.x, hi.y), v);
+          unpack8_bf16(*(const uint4*)(wbl[it] + tid * 16), r8);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = bf2f(f2bf(v[e] + r8[e]));
+          *(uint4*)((T*)a.out[t] + b * a.out_bs[t] + ((int64_t)y * a.Wo + x) * a.outC + c0 + cu * 8) = pack8_bf16(v);
         }
       }
     } else {
