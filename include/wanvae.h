@@ -204,6 +204,19 @@ int wanvae_profile_read(int kind, double *ms, int64_t *launches, double *flops, 
 int wanvae_set_conv_kernel(int kernel);
 
 /*
+ * Norm kernel selection, for testing and tuning. In bf16 the SiLU after an RMS norm (the
+ * residual blocks' norms and norm_out; page 3, "The parts" and "Precision") either runs as
+ * arithmetic or reads a table of its bf16 results over the values of magnitude 2^-16 to 2^16,
+ * built in each workgroup's LDS from the same arithmetic. Both give the same bits.
+ *   mode -1 (default): the table on launches of at least 1,024 blocks of 16 waves, arithmetic
+ *           on smaller ones; 0: arithmetic on every launch; 1: the table on every launch.
+ * Applies to every later norm of any thread. The environment variable WANVAE_NORM_TAB gives the
+ * initial setting. Returns WANVAE_EARG for a mode outside -1..1. Do not change it while another
+ * thread is enqueueing work.
+ */
+int wanvae_set_norm_kernel(int mode);
+
+/*
  * wanvae_decode_tiled -- the spatially tiled decode of the diffusers PR page "Implement tiled
  * VAE encoding/decoding for Wan model": the latent is cut into overlapping spatial tiles, each
  * decoded on its own as wanvae_decode does, and the decoded tiles are blended where they

@@ -314,6 +314,16 @@ def test_full_decode_first_frames_match_oracle_samples(config, mode):
             wanvae.wanvae_set_decode_pipeline(True)
         assert torch.equal(ordered, video)
         del ordered
+        # the norms' SiLU computed on every launch against the default (the LDS table on the
+        # large launches: levels 2 and 3 here), bit for bit
+        say("full decode with the SiLU computed in every norm")
+        wanvae.wanvae_set_norm_kernel(0)
+        try:
+            computed = gpu_decode(z, W, mode)
+        finally:
+            wanvae.wanvae_set_norm_kernel(-1)
+        assert torch.equal(computed, video)
+        del computed
     del video
     torch.cuda.empty_cache()
 

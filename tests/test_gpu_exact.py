@@ -34,18 +34,38 @@ CASES = [
 ]
 
 
-def decode_both(base, B, T, h, w, mode):
-    W = synthetic.exact_sum_weights(base, 21)
-    z = synthetic.normal(21, "latents", (B, synthetic.Z_DIM, T, h, w))
+def inputs(base, B, T, h, w):
+    return synthetic.exact_sum_weights(base, 21), synthetic.normal(21, "latents", (B, synthetic.Z_DIM, T, h, w))
+
+
+def gpu_decode(z, W, mode):
     Wt = {k: torch.from_numpy(v).to(dev()) for k, v in W.items()}
     got = wanvae.wanvae_decode(torch.from_numpy(z).to(dev()), Wt, torch.bfloat16 if mode == "bf16" else torch.float32)
     torch.cuda.synchronize()
-    return to_np(got).astype(np.float64), oracle.decode(z, W, mode).astype(np.float64)
+    return got
 
 
+def decode_both(base, B, T, h, w, mode):
+    W, z = inputs(base, B, T, h, w)
+    return to_np(gpu_decode(z, W, mode)).astype(np.float64), oracle.decode(z, W, mode).astype(np.float64)
+
+
+@pytest.fixture
+def norm_kernel():
+    """Sets the norm kernel for one test and restores the default afterwards."""
+    try:
+        yield wanvae.wanvae_set_norm_kernel
+    finally:
+        wanvae.wanvae_set_norm_kernel(-1)
+
+
+@pytest.mark.parametrize("silu", ["auto", "table"])
 @pytest.mark.parametrize("case", CASES)
-def test_exact_sum_decode_bf16_bit_level(case):
-    say("exact-sum bf16 decode", case)
+def test_exact_sum_decode_bf16_bit_level(case, silu, norm_kernel):
+    """silu = "table": every bf16 norm reads its SiLU from the LDS table (by default only the
+    large launches do, and these decoders have none)."""
+    say("exact-sum bf16 decode", case, silu)
+    norm_kernel(1 if silu == "table" else -1)
     got, want = decode_both(*case, "bf16")
     assert got.shape == want.shape
     d = np.abs(got - want)
@@ -54,6 +74,19 @@ def test_exact_sum_decode_bf16_bit_level(case):
     say(case, "bit-equal", exact, "max diff", d.max(), "max diff / spacing", (d / ulp).max())
     assert exact >= 0.999, exact
     assert d.max() <= 2.0 ** -7, d.max()
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_silu_table_and_arithmetic_give_the_same_bits(case, norm_kernel):
+    """The bf16 decode with every norm's SiLU from the LDS table equals, bit for bit, the decode
+    with every SiLU computed."""
+    say("SiLU table against arithmetic", case)
+    W, z = inputs(*case)
+    norm_kernel(1)
+    tab = gpu_decode(z, W, "bf16")
+    norm_kernel(0)
+    ari = gpu_decode(z, W, "bf16")
+    assert torch.equal(tab, ari)
 
 
 @pytest.mark.parametrize("case", CASES[:2])

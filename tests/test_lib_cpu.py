@@ -208,6 +208,20 @@ def test_decode_pipeline_switch():
         W.wanvae_set_decode_pipeline(True)
 
 
+def test_norm_kernel_switch():
+    L = W.lib()
+    try:
+        for mode in (-1, 0, 1):
+            assert L.wanvae_set_norm_kernel(mode) == W.OK
+        for bad in (-2, 2):
+            assert L.wanvae_set_norm_kernel(bad) == W.EARG
+            assert "-1, 0 or 1" in L.wanvae_last_error().decode()
+            with pytest.raises(ValueError):
+                W.wanvae_set_norm_kernel(bad)
+    finally:
+        W.wanvae_set_norm_kernel(-1)
+
+
 def tiled_ws(tab, n, dtype=W.BF16, B=1, T=31, h=44, w=80, tile=(256, 256), stride=(192, 192)):
     out = ctypes.c_size_t(0)
     rc = W.lib().wanvae_decode_tiled_workspace_size(B, T, h, w, tab, n, dtype, tile[0], tile[1], stride[0], stride[1],

@@ -68,6 +68,7 @@ struct NormArgs {
   const float* gamma;  // [C], rounded to the compute type
   float sqrtC;         // sqrt(C) as a float
   int silu;
+  int tab;             // bf16 SiLU from the LDS table: -1 where the launch is large, 0 never, 1 always
 };
 
 struct AttnArgs {

@@ -1476,23 +1476,46 @@ __global__ void __launch_bounds__(256) k_norm(const NormArgs a) {
   }
 }
 
+// SiLU of the bf16 values u = 0 and 2^-16 <= |u| < 2^16 (but the largest binade's last
+// value), as a table of bf16 results held in LDS: per sign s, entry (s << 12) | 0 for zero and
+// (s << 12) | (|u| bits - kSiluLo + 1) for the others. Each entry is silu_bf16 of its value
+// rounded to bf16 (round to nearest even), the very result the arithmetic path stores, so a
+// lookup and the arithmetic agree bit for bit. Other values (0 < |u| < 2^-16, the largest,
+// inf, NaN) take the arithmetic path. Zero has its own entries because exact zeros are common
+// (a bf16 sum of two opposite values): |u| bits m give the entry max(m - kSiluLo + 1, 0),
+// which is 0 for zero and for the small values, and m - 1 < kSiluLo - 1 flags the small
+// nonzero ones.
+constexpr uint32_t kSiluLo = (127u - 16u) << 7;  // the magnitude bits of 2^-16
+constexpr int kSiluSpan = 4096;                   // zero, then 4,095 magnitudes from 2^-16 on
+constexpr int kSiluEntries = 2 * kSiluSpan;       // both signs: 16 KB
+
 // Bandwidth-oriented version: a position's C channels are spread over LPP lanes, each lane
 // holding VPL 16-byte vectors; a wave covers 64 / LPP positions per round and R rounds, all
 // loads issued before the sums are reduced (xor shuffles within the LPP lanes). bf16 rounds
 // two values per conversion instruction, and the last rounding is the packing store's.
-template <typename T, int LPP, int VPL, int R, bool SILU>
-__global__ void __launch_bounds__(256) k_norm_v(const NormArgs a) {
+// A block is the NWV waves of a workgroup, NWV * PPW * R positions of one frame.
+// TAB (bf16 with SiLU): the workgroup first fills the SiLU table in LDS, then walks the
+// blocks of every frame with a grid stride (two workgroups of 16 waves per CU, so the table is
+// built twice per CU and serves many blocks); without TAB, one block per workgroup and grid
+// y = (frame, batch).
+template <typename T, int LPP, int VPL, int R, bool SILU, bool TAB = false, int NWV = 4>
+__global__ void __launch_bounds__(64 * NWV) k_norm_v(const NormArgs a) {
   using X = Elem<T>;
   constexpr int EV = 16 / (int)sizeof(T);  // elements per 16-byte vector
   constexpr int PPW = 64 / LPP;
   constexpr int CC = LPP * VPL * EV;  // channels of a position
   constexpr bool kSqrtPow2 = CC == 16 || CC == 64 || CC == 256 || CC == 1024;
-  // grid: x = position blocks within a frame, y = (frame t, batch b)
+  static_assert(!TAB || (sizeof(T) == 2 && SILU), "the table holds bf16 SiLU results");
+  __shared__ uint16_t tab[TAB ? kSiluEntries : 1];
   const int lane = threadIdx.x & 63, li = lane % LPP;
-  const int t = blockIdx.y / a.B, b = blockIdx.y % a.B;
-  const int pos0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * PPW * R + lane / LPP;
-  const T* xf = (const T*)a.in[t] + b * a.in_bs[t];
-  T* yf = (T*)a.out[t] + b * a.out_bs[t];
+  if constexpr (TAB) {
+    for (int i = threadIdx.x; i < kSiluEntries; i += 64 * NWV) {
+      const uint32_t j = (uint32_t)(i & (kSiluSpan - 1));
+      const uint32_t h = ((uint32_t)(i >> 12) << 15) | (j ? kSiluLo + j - 1 : 0u);
+      tab[i] = f2bf(silu_bf16(__uint_as_float(h << 16)));
+    }
+    __syncthreads();
+  }
   // this lane's gamma values (its channels are the same in every round)
   float g[VPL][EV];
 #pragma unroll
@@ -1502,94 +1525,143 @@ __global__ void __launch_bounds__(256) k_norm_v(const NormArgs a) {
       const float4 q = *(const float4*)(a.gamma + (v * LPP + li) * EV + e);
       g[v][e] = q.x, g[v][e + 1] = q.y, g[v][e + 2] = q.z, g[v][e + 3] = q.w;
     }
-  uint4 buf[R][VPL];
-  T* outp[R];
+  constexpr int PB = NWV * PPW * R;  // positions per block
+  const int nblk = (a.HW + PB - 1) / PB;
+  const int nall = TAB ? nblk * a.F * a.B : 1;
+  for (int blk = TAB ? (int)blockIdx.x : 0; blk < nall; blk += TAB ? (int)gridDim.x : 1) {
+    const int tb = TAB ? blk / nblk : (int)blockIdx.y;
+    const int pb = TAB ? blk - tb * nblk : (int)blockIdx.x;
+    const int t = tb / a.B, b = tb % a.B;
+    const int pos0 = (pb * NWV + (int)(threadIdx.x >> 6)) * PPW * R + lane / LPP;
+    const T* xf = (const T*)a.in[t] + b * a.in_bs[t];
+    T* yf = (T*)a.out[t] + b * a.out_bs[t];
+    uint4 buf[R][VPL];
+    T* outp[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int pos = pos0 + r * PPW;
-    outp[r] = nullptr;
-    if (pos < a.HW) {
-      const T* x = xf + (int64_t)pos * a.C;
-      outp[r] = yf + (int64_t)pos * a.C;
+    for (int r = 0; r < R; ++r) {
+      const int pos = pos0 + r * PPW;
+      outp[r] = nullptr;
+      if (pos < a.HW) {
+        const T* x = xf + (int64_t)pos * a.C;
+        outp[r] = yf + (int64_t)pos * a.C;
 #pragma unroll
-      for (int v = 0; v < VPL; ++v) buf[r][v] = *(const uint4*)(x + (v * LPP + li) * EV);
-    } else {
-#pragma unroll
-      for (int v = 0; v < VPL; ++v) buf[r][v] = make_uint4(0, 0, 0, 0);
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    float val[VPL][EV];
-    // bf16: the sum of squares in float64, so that ||x|| and x / ||x|| are exact to far below
-    // the bf16 rounding that follows; fp32: in float32
-    using Acc = typename std::conditional<sizeof(T) == 2, double, float>::type;
-    Acc ss = 0;
-#pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-      if constexpr (sizeof(T) == 2) {
-        unpack8_bf16(buf[r][v], val[v]);
+        for (int v = 0; v < VPL; ++v) buf[r][v] = *(const uint4*)(x + (v * LPP + li) * EV);
       } else {
-        val[v][0] = __uint_as_float(buf[r][v].x), val[v][1] = __uint_as_float(buf[r][v].y);
-        val[v][2] = __uint_as_float(buf[r][v].z), val[v][3] = __uint_as_float(buf[r][v].w);
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) buf[r][v] = make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float val[VPL][EV];
+      // bf16: the sum of squares in float64, so that ||x|| and x / ||x|| are exact to far below
+      // the bf16 rounding that follows; fp32: in float32
+      using Acc = typename std::conditional<sizeof(T) == 2, double, float>::type;
+      Acc ss = 0;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        if constexpr (sizeof(T) == 2) {
+          unpack8_bf16(buf[r][v], val[v]);
+        } else {
+          val[v][0] = __uint_as_float(buf[r][v].x), val[v][1] = __uint_as_float(buf[r][v].y);
+          val[v][2] = __uint_as_float(buf[r][v].z), val[v][3] = __uint_as_float(buf[r][v].w);
+        }
+#pragma unroll
+        for (int e = 0; e < EV; ++e) ss += (Acc)val[v][e] * (Acc)val[v][e];
       }
 #pragma unroll
-      for (int e = 0; e < EV; ++e) ss += (Acc)val[v][e] * (Acc)val[v][e];
-    }
+      for (int off = LPP / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+      if (!outp[r]) continue;
+      const float d = fmaxf(sqrtf((float)ss), 1e-12f);
+      // bf16: 1 / max(||x||, 1e-12) in float64, carried as two floats ih + il
+      const double dinv = fmin(rsqrt((double)ss), 1e12);
+      const float ih = (float)dinv, il = (float)(dinv - (double)ih);
 #pragma unroll
-    for (int off = LPP / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
-    if (!outp[r]) continue;
-    const float d = fmaxf(sqrtf((float)ss), 1e-12f);
-    // bf16: 1 / max(||x||, 1e-12) in float64, carried as two floats ih + il
-    const double dinv = fmin(rsqrt((double)ss), 1e12);
-    const float ih = (float)dinv, il = (float)(dinv - (double)ih);
+      for (int v = 0; v < VPL; ++v) {
+        const int c0 = (v * LPP + li) * EV;
+        float o[EV];
+        if constexpr (sizeof(T) == 2) {
+          // bf16: x / ||x|| as x ih + x il, rounded once (to within 2^-47 of the float64
+          // quotient, then to float32 and bf16, as a float64 value is cast to bf16); the
+          // products by sqrt(C) and gamma in float32 (exact before their rounding); SiLU to
+          // about one float32 ulp (silu_bf16). A float32 result then lands on the far side of a
+          // bf16 rounding boundary from the exact value only where it lies within about an ulp
+          // of that boundary.
+          auto round2 = [](float& p, float& q) {
+            const uint32_t w = pack2_bf16(p, q);
+            p = __uint_as_float(w << 16);
+            q = __uint_as_float(w & 0xffff0000u);
+          };
+          if constexpr (TAB) {
+            // R(u gamma) for the vector's EV values, packed; then one table read per value
+            // when every value of this lane's vector is in the table's range
+            uint32_t w[EV / 2];
+            uint32_t hi_m = 0, lo_m1 = 0xffffffffu;  // max entry offset, min (|u| bits - 1)
+            uint32_t ia[EV];
 #pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-      const int c0 = (v * LPP + li) * EV;
-      float o[EV];
-      if constexpr (sizeof(T) == 2) {
-        // bf16: x / ||x|| as x ih + x il, rounded once (to within 2^-47 of the float64
-        // quotient, then to float32 and bf16, as a float64 value is cast to bf16); the
-        // products by sqrt(C) and gamma in float32 (exact before their rounding); SiLU to
-        // about one float32 ulp (silu_bf16). A float32 result then lands on the far side of a
-        // bf16 rounding boundary from the exact value only where it lies within about an ulp
-        // of that boundary.
-        auto round2 = [](float& p, float& q) {
-          const uint32_t w = pack2_bf16(p, q);
-          p = __uint_as_float(w << 16);
-          q = __uint_as_float(w & 0xffff0000u);
-        };
+            for (int e = 0; e < EV; e += 2) {
+              float u0 = __builtin_fmaf(val[v][e], ih, val[v][e] * il);
+              float u1 = __builtin_fmaf(val[v][e + 1], ih, val[v][e + 1] * il);
+              round2(u0, u1);
+              u0 *= a.sqrtC, u1 *= a.sqrtC;
+              if constexpr (!kSqrtPow2) round2(u0, u1);
+              w[e / 2] = pack2_bf16(u0 * g[v][e], u1 * g[v][e + 1]);
 #pragma unroll
-        for (int e = 0; e < EV; e += 2) {
-          float u0 = __builtin_fmaf(val[v][e], ih, val[v][e] * il);
-          float u1 = __builtin_fmaf(val[v][e + 1], ih, val[v][e + 1] * il);
-          round2(u0, u1);
-          u0 *= a.sqrtC, u1 *= a.sqrtC;
-          // C = 16, 64, 256, 1024: sqrt(C) is a power of two, the product exact, its rounding
-          // the identity
-          if constexpr (!kSqrtPow2) round2(u0, u1);
-          u0 *= g[v][e], u1 *= g[v][e + 1];
-          if constexpr (SILU) {
-            round2(u0, u1);
-            u0 = silu_bf16(u0);
-            u1 = silu_bf16(u1);
+              for (int k = 0; k < 2; ++k) {
+                const uint32_t h = k ? w[e / 2] >> 16 : w[e / 2] & 0xffffu;
+                const uint32_t mag = h & 0x7fffu;
+                const uint32_t m = mag > kSiluLo - 1u ? mag - (kSiluLo - 1u) : 0u;
+                hi_m = max(hi_m, m);
+                lo_m1 = min(lo_m1, mag - 1u);     // zero wraps to the top
+                ia[e + k] = ((h >> 15) << 12) | m;  // read only when every m is below the span
+              }
+            }
+            uint4 res;
+            uint32_t* rw = (uint32_t*)&res;
+            if (hi_m < (uint32_t)kSiluSpan && lo_m1 >= kSiluLo - 1u) {
+#pragma unroll
+              for (int e = 0; e < EV; e += 2) rw[e / 2] = (uint32_t)tab[ia[e]] | ((uint32_t)tab[ia[e + 1]] << 16);
+            } else {
+#pragma unroll
+              for (int e = 0; e < EV; ++e) o[e] = silu_bf16(__uint_as_float(e & 1 ? w[e / 2] & 0xffff0000u : w[e / 2] << 16));
+              res = pack8_bf16(o);
+            }
+            *(uint4*)(outp[r] + c0) = res;
+            continue;
+          } else {
+#pragma unroll
+            for (int e = 0; e < EV; e += 2) {
+              float u0 = __builtin_fmaf(val[v][e], ih, val[v][e] * il);
+              float u1 = __builtin_fmaf(val[v][e + 1], ih, val[v][e + 1] * il);
+              round2(u0, u1);
+              u0 *= a.sqrtC, u1 *= a.sqrtC;
+              // C = 16, 64, 256, 1024: sqrt(C) is a power of two, the product exact, its
+              // rounding the identity
+              if constexpr (!kSqrtPow2) round2(u0, u1);
+              u0 *= g[v][e], u1 *= g[v][e + 1];
+              if constexpr (SILU) {
+                round2(u0, u1);
+                u0 = silu_bf16(u0);
+                u1 = silu_bf16(u1);
+              }
+              o[e] = u0, o[e + 1] = u1;  // rounded by the packing store
+            }
           }
-          o[e] = u0, o[e + 1] = u1;  // rounded by the packing store
-        }
-      } else {
+        } else {
 #pragma unroll
-        for (int e = 0; e < EV; ++e) {
-          float u = val[v][e] / d;
-          u = u * a.sqrtC;
-          u = u * g[v][e];
-          if constexpr (SILU) u = u / (1.f + expf(-u));
-          o[e] = u;
+          for (int e = 0; e < EV; ++e) {
+            float u = val[v][e] / d;
+            u = u * a.sqrtC;
+            u = u * g[v][e];
+            if constexpr (SILU) u = u / (1.f + expf(-u));
+            o[e] = u;
+          }
         }
-      }
-      if constexpr (sizeof(T) == 2) {
-        *(uint4*)(outp[r] + c0) = pack8_bf16(o);
-      } else {
-        *(float4*)(outp[r] + c0) = make_float4(o[0], o[1], o[2], o[3]);
+        if constexpr (sizeof(T) == 2) {
+          *(uint4*)(outp[r] + c0) = pack8_bf16(o);
+        } else {
+          *(float4*)(outp[r] + c0) = make_float4(o[0], o[1], o[2], o[3]);
+        }
       }
     }
   }
@@ -2423,6 +2495,16 @@ hipError_t launch_conv(const ConvArgs& a, int dtype, int tile, hipStream_t s) {
 template <typename T, int LPP, int VPL>
 static hipError_t norm_v_go(const NormArgs& a, hipStream_t s) {
   constexpr int R = 4;
+  if constexpr (sizeof(T) == 2) {
+    // bf16 with SiLU over at least two rounds of 16-wave blocks (or where asked for): the
+    // table variant, two workgroups per CU
+    constexpr int TPB = 16 * (64 / LPP) * R;
+    const int64_t nall = (int64_t)((a.HW + TPB - 1) / TPB) * a.F * a.B;
+    if (a.silu && (a.tab > 0 || (a.tab < 0 && nall >= 1024))) {
+      hipLaunchKernelGGL((k_norm_v<T, LPP, VPL, R, true, true, 16>), dim3(512), dim3(1024), 0, s, a);
+      return hipGetLastError();
+    }
+  }
   const int per_block = 4 * (64 / LPP) * R;
   const dim3 grid((unsigned)((a.HW + per_block - 1) / per_block), (unsigned)(a.F * a.B));
   if (a.silu)

@@ -346,6 +346,14 @@ static std::atomic<int> g_conv_kernel{[] {
   return k >= -1 && k < WANVAE_CONV_KERNELS ? k : -1;
 }()};
 
+// The bf16 norm's SiLU: -1 automatic (the LDS table on large launches), 0 arithmetic only,
+// 1 the table on every launch. WANVAE_NORM_TAB gives the initial setting.
+static std::atomic<int> g_norm_kernel{[] {
+  const char* e = getenv("WANVAE_NORM_TAB");
+  const int k = e ? atoi(e) : -1;
+  return k >= -1 && k <= 1 ? k : -1;
+}()};
+
 static int pick_tile(const ConvArgs& a, int dtype) {
   const int forced = g_conv_kernel.load(std::memory_order_relaxed);
   const int Cout = a.Cout;
@@ -540,6 +548,7 @@ static int run_norm(const FrameRef& in, const FrameRef& out, int F, int B, int H
   n.gamma = gamma;
   n.sqrtC = (float)std::sqrt((double)C);
   n.silu = silu ? 1 : 0;
+  n.tab = g_norm_kernel.load(std::memory_order_relaxed);
   hipEvent_t e0 = prof_start(st);
   HIP_TRY(launch_norm(n, dtype, st));
   prof_stop(e0, WANVAE_KNORM, 0, 2.0 * F * B * (double)HW * C * esize(dtype), st);
@@ -1054,13 +1063,19 @@ int wanvae_set_conv_kernel(int kernel) {
   return WANVAE_OK;
 }
 
+int wanvae_set_norm_kernel(int mode) {
+  if (mode < -1 || mode > 1) return fail(WANVAE_EARG, "norm kernel %d is not -1, 0 or 1", mode);
+  g_norm_kernel.store(mode);
+  return WANVAE_OK;
+}
+
 int wanvae_set_decode_pipeline(int on) {
   if (on != 0 && on != 1) return fail(WANVAE_EARG, "decode pipeline switch %d is not 0 or 1", on);
   g_pipeline.store(on);
   return WANVAE_OK;
 }
 
-int wanvae_version(void) { return 200; }
+int wanvae_version(void) { return 201; }
 
 int wanvae_decode_workspace_size(int64_t B, int64_t T, int64_t h, int64_t w, const wanvae_tensor* weights,
                                  int64_t n_weights, int32_t dtype, size_t* bytes) {

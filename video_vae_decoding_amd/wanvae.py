@@ -74,13 +74,15 @@ def lib() -> ctypes.CDLL:
         L.wanvae_version.argtypes = []
         L.wanvae_set_conv_kernel.argtypes = [ctypes.c_int]
         L.wanvae_set_decode_pipeline.argtypes = [ctypes.c_int]
+        L.wanvae_set_norm_kernel.argtypes = [ctypes.c_int]
         L.wanvae_decode_tiled_workspace_size.argtypes = [i64, i64, i64, i64, T, i64, i32, i32, i32, i32, i32,
                                                          ctypes.POINTER(sz)]
         L.wanvae_decode_tiled.argtypes = [vp, i32, i64, i64, i64, i64, T, i64, i32, i32, i32, i32, i32, vp, vp, sz, vp]
         for f in ("wanvae_decode_workspace_size", "wanvae_decode", "wanvae_causal_conv3d_workspace_size",
                   "wanvae_causal_conv3d", "wanvae_causal_conv3d_noalloc", "wanvae_attn_block_workspace_size", "wanvae_attn_block", "wanvae_version",
                   "wanvae_profile_enable", "wanvae_profile_read", "wanvae_set_conv_kernel",
-                  "wanvae_set_decode_pipeline", "wanvae_decode_tiled_workspace_size", "wanvae_decode_tiled"):
+                  "wanvae_set_decode_pipeline", "wanvae_set_norm_kernel", "wanvae_decode_tiled_workspace_size",
+                  "wanvae_decode_tiled"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -456,6 +458,12 @@ CONV_KERNELS = 14
 def wanvae_set_conv_kernel(kernel: int) -> None:
     """Use conv kernel ``kernel`` wherever it can run a conv (-1: each conv's default)."""
     check(lib().wanvae_set_conv_kernel(kernel))
+
+
+def wanvae_set_norm_kernel(mode: int) -> None:
+    """bf16 SiLU after the RMS norm: from the LDS table on large launches (-1, the default),
+    arithmetic only (0) or the table on every launch (1). The results are the same bits."""
+    check(lib().wanvae_set_norm_kernel(mode))
 
 
 def wanvae_set_decode_pipeline(on: bool) -> None:
