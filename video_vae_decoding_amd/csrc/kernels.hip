@@ -14,8 +14,9 @@
 //               DupUp3D add, the time conv's channel->frame interleave, unpatchify + clamp,
 //               and the q/k/v split.
 //  k_norm_v     WanRMS_norm (+ SiLU) per position; the bf16 chain is evaluated to about a
-//               float32 ulp before each bf16 rounding, which leaves it VALU-issue bound just
-//               ahead of HBM.
+//               float32 ulp before each bf16 rounding. On large launches the bf16 SiLU comes
+//               from a table of its results in LDS, which leaves the pass streaming at about
+//               the device-copy rate.
 //  k_attn_mm    bf16 single-head attention over the h*w positions of a frame on materialised
 //  k_attn_fac   scores: the scores GEMM with each 128-key tile's softmax in its epilogue (P
 //               stored in bf16), the per-tile weights, and the P V GEMM with a running rescale.
