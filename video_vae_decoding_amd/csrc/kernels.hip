@@ -427,6 +427,14 @@ __device__ __forceinline__ void epilogue8_bf16(const ConvArgs& a, int t, int b, 
     if (a.dup_r == 4 * a.dup_ft) {
       // each input channel repeated over exactly the (ft, 2, 2) sub-positions: channel c
       unpack8_bf16(*(const uint4*)(d + c), dv);
+    } else if (2 * a.dup_r == 4 * a.dup_ft) {
+      // twice the input channels of the output (up block 2): output channel c + e takes input
+      // channel 2 (c + e) + sub / r, every other one of the 16 from 2c on (32 bytes, aligned)
+      const uint4 q0 = *(const uint4*)(d + 2 * c), q1 = *(const uint4*)(d + 2 * c + 8);
+      const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+      const bool odd = sub >= a.dup_r;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dv[e] = __uint_as_float(odd ? w[e] & 0xffff0000u : w[e] << 16);
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) dv[e] = bf2f(d[(4 * a.dup_ft * (c + e) + sub) / a.dup_r].u);
