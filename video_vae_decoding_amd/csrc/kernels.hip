@@ -410,6 +410,13 @@ __device__ __forceinline__ void unpack8_bf16(const uint4 r, float v[8]) {
   }
 }
 
+// A 16-byte store marked non-temporal (streamed past the caches' keep policy): a conv's
+// output is not read again before it leaves L2.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void st16_nt(void* p, const uint4 v) {
+  __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, (u32x4_t*)p);
+}
+
 __device__ __forceinline__ void epilogue8_bf16(const ConvArgs& a, int t, int b, int y, int x, int c, float v[8]) {
   using T = bf16_t;
   const int64_t pix = (int64_t)y * a.Wo + x;
@@ -443,10 +450,10 @@ __device__ __forceinline__ void epilogue8_bf16(const ConvArgs& a, int t, int b, 
     for (int e = 0; e < 8; ++e) v[e] = bf2f(f2bf(v[e] + dv[e]));
   }
   if (a.mode == kEpiFrames) {
-    *(uint4*)((T*)a.out[t] + b * a.out_bs[t] + pix * a.outC + c) = pack8_bf16(v);
+    st16_nt((T*)a.out[t] + b * a.out_bs[t] + pix * a.outC + c, pack8_bf16(v));
   } else if (a.mode == kEpiInterleave) {
     const int half = c >= a.outC ? 1 : 0, fr = 2 * t + half;
-    *(uint4*)((T*)a.out[fr] + b * a.out_bs[fr] + pix * a.outC + (c - half * a.outC)) = pack8_bf16(v);
+    st16_nt((T*)a.out[fr] + b * a.out_bs[fr] + pix * a.outC + (c - half * a.outC), pack8_bf16(v));
   } else if (a.mode == kEpiQKV) {
     const int C = a.outC, fr = t * a.B + b;
     if (c < 2 * C) {
@@ -1394,7 +1401,7 @@ __global__ void __launch_bounds__(64 * WGC * WGP, 1) k_conv_halo(const ConvArgs 
           unpack8_bf16(*(const uint4*)(wbl[it] + tid * 16), r8);
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = bf2f(f2bf(v[e] + r8[e]));
-          *(uint4*)((T*)a.out[t] + b * a.out_bs[t] + ((int64_t)y * a.Wo + x) * a.outC + c0 + cu * 8) = pack8_bf16(v);
+          st16_nt((T*)a.out[t] + b * a.out_bs[t] + ((int64_t)y * a.Wo + x) * a.outC + c0 + cu * 8, pack8_bf16(v));
         }
       }
     } else {
